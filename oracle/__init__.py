@@ -1,0 +1,12 @@
+"""Float64 CPU oracle of the PPSA decode step -- test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package. It shares no code with the HIP library.
+"""
+from .ppsa_oracle import (FULL, FULL_SELECT, SPARSE, attend, decode_layer, decode_step, default_scale,
+                          full_attention, logits, select_topk, selection_scores, softmax_weights,
+                          sparse_attention, widen)
+
+__all__ = ["FULL", "FULL_SELECT", "SPARSE", "attend", "decode_layer", "decode_step", "default_scale",
+           "full_attention", "logits", "select_topk", "selection_scores", "softmax_weights",
+           "sparse_attention", "widen"]

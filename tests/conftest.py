@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def _ensure_synth():
+    import synth
+    if not os.path.exists(os.path.join(ROOT, "synth", "libppsa_synth.so")):
+        synth.build()
+
+
+_ensure_synth()
+
+
+@pytest.fixture(scope="session")
+def root():
+    return ROOT

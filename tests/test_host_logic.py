@@ -1,0 +1,45 @@
+"""Host-side logic: byte accounting and schedules, against the page's figures."""
+import json
+import os
+
+import numpy as np
+
+from synth import WORKLOADS, kv_cache_bytes, schedule_for, step_kv_bytes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_kv_cache_size_page_example():
+    g = json.load(open(os.path.join(GOLDEN, "kv_cache_size.json")))
+    got = kv_cache_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["tokens"], g["bytes_per_element"])
+    assert got == g["printed_total_bytes_binary"] == 64 * 2 ** 30
+
+
+def test_schedule_matches_framework_figure():
+    g = json.load(open(os.path.join(GOLDEN, "decode_schedule.json")))
+    for ex in g["examples"]:
+        assert "".join(schedule_for(ex["layers"], (2, ex["middle"]))) == ex["kinds"]
+
+
+def test_two_selections_per_step():
+    for wl in WORKLOADS.values():
+        sched = wl.schedule()
+        assert sched.count("X") == 2
+        assert sched[0] == sched[1] == "F"
+        assert sched.index("X") == 2
+
+
+def test_step_bytes_fixed_length_workloads():
+    want = {"tiny-f32": 17825792, "llama2-7b-10k": 905969664, "llama3-8b-gqa-32k": 4026531840,
+            "llama2-7b-100k": 7650410496}
+    for name, b in want.items():
+        wl = WORKLOADS[name]
+        assert step_kv_bytes(wl, [wl.max_len] * wl.batch) == b
+
+
+def test_step_bytes_ragged():
+    wl = WORKLOADS["llama3-70b-ragged-10k"]
+    lens = np.full(wl.batch, 9216)
+    per_full = 2 * wl.batch * wl.kv_heads * 9216 * 256
+    per_sparse = 2 * wl.batch * wl.kv_heads * 256 * 256
+    assert step_kv_bytes(wl, lens) == 4 * per_full + 76 * per_sparse == 1845493760
