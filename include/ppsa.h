@@ -1,0 +1,152 @@
+/*
+ * ppsa.h -- C ABI of the PPSA (position persistent sparse attention) decode
+ * step for AMD Instinct MI355X (gfx950).
+ *
+ * The method is TidalDecode's, as described on the paper-review page
+ * "TidalDecode: Fast and Accurate LLM Decoding with Position Persistent Sparse
+ * Attention" (arXiv 2410.05076):
+ *   - section 3, PPSA paragraph, attention equation: per query head,
+ *     A = q K^T * scale and H = softmax(A) V, scale = 1/sqrt(head_dim);
+ *   - section 2, solution overview, and section 3, decode-step framework
+ *     figure: each decode step runs full attention in its first layers, full
+ *     attention plus top-k token selection at two layers, and sparse
+ *     attention over the most recently selected positions everywhere else;
+ *   - section 3, PPSA paragraph: a sparse layer reuses the positions of the
+ *     preceding selection layer.
+ * Readings where the page is silent: the selection score of a position is
+ * the float32 sum, over the query heads sharing a KV head, of its raw logit
+ * q.k*scale; one set is selected per (batch row, KV head); equal scores go to
+ * the lower position; a sparse layer renormalises over its positions.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns all
+ *     memory; the library never allocates, frees or synchronises. Every call
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns before they finish.
+ *   - Layouts are dense row-major: q and out [B, Hq, d]; K and V caches
+ *     [B, Hkv, Nmax, d] (one row of d elements per position); seq_lens [B]
+ *     int32; scores [B, Hkv, Nmax] float32; idx [B, Hkv, topk] int32. q, K,
+ *     V and out share the element type `dtype`. Query head hq uses KV head
+ *     hq / (Hq / Hkv).
+ *   - q, K, V, out and the workspace must be 16-byte aligned.
+ *   - Device-side lengths: seq_lens[b] is clamped into [0, Nmax]. Rows at or
+ *     past it are never read. A unit with no live rows outputs zeros and
+ *     selects nothing.
+ *   - Errors: every argument is checked on the host before any HIP call. A
+ *     failing check returns a negative ppsa_status and enqueues nothing. A
+ *     failed launch returns PPSA_ERR_HIP. The library never aborts or throws.
+ *   - Calls are stateless. Concurrent calls must use distinct workspaces.
+ */
+#ifndef PPSA_H
+#define PPSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PPSA_ABI_VERSION 1
+
+typedef enum ppsa_status {
+  PPSA_OK = 0,
+  PPSA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or count */
+  PPSA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim, group size, dtype */
+  PPSA_ERR_WORKSPACE = -3,   /* workspace smaller than ppsa_workspace_bytes() */
+  PPSA_ERR_SCHEDULE = -4,    /* decode schedule: unknown kind, or sparse before any selection */
+  PPSA_ERR_HIP = -5          /* a kernel launch failed */
+} ppsa_status;
+
+typedef enum ppsa_dtype { PPSA_F32 = 0, PPSA_BF16 = 1 } ppsa_dtype;
+
+typedef enum ppsa_layer_kind { PPSA_FULL = 0, PPSA_FULL_SELECT = 1, PPSA_SPARSE = 2 } ppsa_layer_kind;
+
+typedef struct ppsa_dims {
+  int32_t batch;        /* B >= 0; B == 0 makes every call a no-op returning PPSA_OK */
+  int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads, Hq/Hkv <= 16 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t max_seq_len;  /* Nmax >= 1: cache rows per (batch row, KV head) */
+  int32_t dtype;        /* ppsa_dtype of q, K, V and out */
+  float scale;          /* logit scale; 0 means 1/sqrt(head_dim) */
+} ppsa_dims;
+
+/* Library ABI version (PPSA_ABI_VERSION). */
+int ppsa_abi_version(void);
+
+/* Static text for a status code. */
+const char* ppsa_status_string(int status);
+
+/*
+ * Workspace bytes any single call below needs for these dims and token
+ * budget (topk), including ppsa_decode_step. Pure host function; returns 0
+ * for invalid dims.
+ */
+size_t ppsa_workspace_bytes(const ppsa_dims* dims, int32_t topk);
+
+/*
+ * Full attention (section 3 attention equation; the "full attention" layer
+ * kind of the section 3 framework figure): for every (b, hq),
+ *   out[b,hq,:] = sum_n softmax_n(q[b,hq].K[b,kv,n] * scale) V[b,kv,n,:]
+ * over the live rows n in [0, seq_lens[b]), kv = hq / (Hq/Hkv).
+ */
+int ppsa_full_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Full attention plus token selection (the selection layer kind of the
+ * section 3 framework figure; top-k by attention score, section 2 solution
+ * overview). Writes `out` as ppsa_full_attn, and for every (b, kv):
+ *   scores[b,kv,n] = sum over the group's query heads of q.K[n]*scale (float32)
+ *                    for live n; entries past seq_lens[b] are left untouched;
+ *   idx[b,kv,:]    = the k_eff = min(topk, seq_lens[b]) live positions with
+ *                    the highest score, equal scores to the lower position,
+ *                    in ascending position order, slots k_eff..topk-1 = -1.
+ * `scores` may be NULL (the workspace then holds them). 1 <= topk <= Nmax.
+ */
+int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, int32_t topk, void* out, float* scores, int32_t* idx,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Token selection alone, on given scores [B, Hkv, Nmax] (float32, only the
+ * live entries are read): writes idx exactly as ppsa_full_attn_select does.
+ * Scores must not be NaN. -0.0 ranks equal to +0.0.
+ */
+int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
+                     int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse attention over pre-selected positions (the PPSA layer kind, section
+ * 3 PPSA paragraph): attention of every query head of KV group kv over the
+ * rows idx[b,kv,0..topk) only, renormalised over them. Entries outside
+ * [0, seq_lens[b]) are skipped; a repeated entry counts once per occurrence;
+ * a unit with no valid entry outputs zeros.
+ */
+int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const int32_t* idx, int32_t topk, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step over `num_layers` layers (section 3 framework figure):
+ * layer l runs the kind schedule[l] (host array of ppsa_layer_kind values)
+ * on q[l], K[l], V[l] and writes out[l]. A PPSA_FULL_SELECT layer writes the
+ * next slot of `idx`; a PPSA_SPARSE layer reads the most recently written
+ * slot. A sparse layer before any selection returns PPSA_ERR_SCHEDULE.
+ *   q, out:        [L, B, Hq, d]
+ *   k/v_cache:     [L, B, Hkv, Nmax, d]
+ *   idx:           [S, B, Hkv, topk], S = number of PPSA_FULL_SELECT layers
+ *                  (may be NULL when S == 0)
+ *   scores:        [S, B, Hkv, Nmax] float32, or NULL
+ * seq_lens is shared by all layers. 1 <= topk <= Nmax when S > 0.
+ */
+int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
+                     int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PPSA_H */

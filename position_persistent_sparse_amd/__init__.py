@@ -1,0 +1,206 @@
+"""Python binding of libppsa.so, the PPSA decode-step library for MI355X.
+
+Argument marshalling only: every function checks tensor shapes, dtypes and
+devices, then calls the C entry point of the same name (include/ppsa.h) with
+raw device pointers and torch's current HIP stream. All arithmetic happens in
+the library's HIP kernels; if the library is missing, import fails loudly.
+
+Tensors: q/out [B, Hq, d]; k_cache/v_cache [B, Hkv, Nmax, d] (bfloat16 or
+float32, contiguous, on the GPU); seq_lens [B] int32; idx [B, Hkv, topk]
+int32; scores [B, Hkv, Nmax] float32. decode_step takes the same tensors
+with a leading layer axis.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libppsa.so")
+
+PPSA_OK, PPSA_ERR_INVALID_ARG, PPSA_ERR_UNSUPPORTED = 0, -1, -2
+PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
+PPSA_F32, PPSA_BF16 = 0, 1
+PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
+KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class PPSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    dp = ctypes.POINTER(Dims)
+    lib.ppsa_abi_version.restype = ctypes.c_int
+    lib.ppsa_status_string.argtypes = [ctypes.c_int]
+    lib.ppsa_status_string.restype = ctypes.c_char_p
+    lib.ppsa_workspace_bytes.argtypes = [dp, i32]
+    lib.ppsa_workspace_bytes.restype = sz
+    lib.ppsa_full_attn.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ppsa_full_attn_select.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.ppsa_select_topk.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
+    lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
+                 "ppsa_decode_step"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return _lib.ppsa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.ppsa_status_string(int(status)).decode()
+
+
+def make_dims(batch, q_heads, kv_heads, head_dim, max_seq_len, dtype, scale: float = 0.0) -> Dims:
+    code = {torch.float32: PPSA_F32, torch.bfloat16: PPSA_BF16}.get(dtype, dtype)
+    return Dims(int(batch), int(q_heads), int(kv_heads), int(head_dim), int(max_seq_len), int(code), float(scale))
+
+
+def workspace_bytes(dims: Dims, topk: int = 0) -> int:
+    return int(_lib.ppsa_workspace_bytes(ctypes.byref(dims), int(topk)))
+
+
+def alloc_workspace(dims: Dims, topk: int = 0, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(dims, topk), 16), dtype=torch.uint8, device=device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != PPSA_OK:
+        raise PPSAError(status, where)
+
+
+def _dims_of(q, k_cache, scale, layered=False):
+    if layered:
+        _, B, Hq, d = q.shape
+        _, _, Hkv, N, _ = k_cache.shape
+    else:
+        B, Hq, d = q.shape
+        _, Hkv, N, _ = k_cache.shape
+    return make_dims(B, Hq, Hkv, d, N, q.dtype, scale)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(q, k_cache, v_cache, seq_lens, layered=False):
+    nd = 4 if layered else 3
+    _require(q.dim() == nd and k_cache.dim() == nd + 1, "q must be [(L,) B, Hq, d] and K [(L,) B, Hkv, N, d]")
+    _require(k_cache.shape == v_cache.shape, "K and V shapes differ")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q, K and V must share a dtype")
+    _require(q.shape[-1] == k_cache.shape[-1], "head_dim mismatch")
+    _require(q.shape[-3] == k_cache.shape[-4], "batch mismatch")
+    if layered:
+        _require(q.shape[0] == k_cache.shape[0], "layer count mismatch")
+    for t in (q, k_cache, v_cache, seq_lens):
+        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous GPU tensors")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.shape == (q.shape[-3],), "seq_lens must be int32 [B]")
+
+
+def full_attn(q, k_cache, v_cache, seq_lens, out=None, workspace=None, scale: float = 0.0):
+    _check_tensors(q, k_cache, v_cache, seq_lens)
+    dims = _dims_of(q, k_cache, scale)
+    out = torch.empty_like(q) if out is None else out
+    ws = alloc_workspace(dims, 0, q.device) if workspace is None else workspace
+    _check(_lib.ppsa_full_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                               _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)), "ppsa_full_attn")
+    return out
+
+
+def full_attn_select(q, k_cache, v_cache, seq_lens, topk: int, out=None, scores=None, idx=None, workspace=None,
+                     scale: float = 0.0):
+    _check_tensors(q, k_cache, v_cache, seq_lens)
+    dims = _dims_of(q, k_cache, scale)
+    out = torch.empty_like(q) if out is None else out
+    if idx is None:
+        idx = torch.empty((dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
+    ws = alloc_workspace(dims, topk, q.device) if workspace is None else workspace
+    _check(_lib.ppsa_full_attn_select(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                      int(topk), _ptr(out), _ptr(scores), _ptr(idx), _ptr(ws), ws.numel(),
+                                      _stream(q.device)), "ppsa_full_attn_select")
+    return out, idx
+
+
+def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None):
+    _require(scores.dim() == 3 and scores.dtype == torch.float32 and scores.is_contiguous() and scores.is_cuda,
+             "scores must be contiguous float32 [B, Hkv, N] on the GPU")
+    B, Hkv, N = scores.shape
+    dims = make_dims(B, num_q_heads or Hkv, Hkv, 128, N, PPSA_F32)
+    if idx is None:
+        idx = torch.empty((B, Hkv, int(topk)), dtype=torch.int32, device=scores.device)
+    _check(_lib.ppsa_select_topk(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), int(topk), _ptr(idx), None, 0,
+                                 _stream(scores.device)), "ppsa_select_topk")
+    return idx
+
+
+def sparse_attn(q, k_cache, v_cache, seq_lens, idx, out=None, workspace=None, scale: float = 0.0):
+    _check_tensors(q, k_cache, v_cache, seq_lens)
+    dims = _dims_of(q, k_cache, scale)
+    _require(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 3
+             and tuple(idx.shape[:2]) == (dims.batch, dims.num_kv_heads), "idx must be int32 [B, Hkv, topk]")
+    topk = idx.shape[2]
+    out = torch.empty_like(q) if out is None else out
+    ws = alloc_workspace(dims, topk, q.device) if workspace is None else workspace
+    _check(_lib.ppsa_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                 _ptr(idx), int(topk), _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)),
+           "ppsa_sparse_attn")
+    return out
+
+
+def schedule_codes(schedule) -> ctypes.Array:
+    codes = [KIND_CODES[k] if isinstance(k, str) else int(k) for k in schedule]
+    return (ctypes.c_int32 * max(len(codes), 1))(*codes)
+
+
+def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, idx=None, scores=None,
+                workspace=None, scale: float = 0.0, sched_codes=None):
+    """One decode step; returns (out [L,B,Hq,d], idx [S,B,Hkv,topk]) with S = selection layers."""
+    _check_tensors(q, k_cache, v_cache, seq_lens, layered=True)
+    dims = _dims_of(q, k_cache, scale, layered=True)
+    L = q.shape[0]
+    _require(len(schedule) == L, "schedule length must equal the layer count")
+    n_sel = sum(1 for k in schedule if k in ("X", PPSA_FULL_SELECT))
+    out = torch.empty_like(q) if out is None else out
+    if idx is None and n_sel:
+        idx = torch.empty((n_sel, dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
+    ws = alloc_workspace(dims, topk if n_sel else 0, q.device) if workspace is None else workspace
+    codes = schedule_codes(schedule) if sched_codes is None else sched_codes
+    _check(_lib.ppsa_decode_step(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_lens), int(topk), _ptr(out), _ptr(idx), _ptr(scores), _ptr(ws),
+                                 ws.numel(), _stream(q.device)), "ppsa_decode_step")
+    return out, idx
+
+
+def raw_library():
+    """The ctypes handle itself, for callers that manage pointers directly."""
+    return _lib

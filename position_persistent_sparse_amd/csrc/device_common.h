@@ -1,0 +1,77 @@
+// Device helpers for the gfx950 kernels: bf16 packing, DPP reductions,
+// workgroup scans. Wave size is 64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ppsa {
+
+constexpr int kWave = 64;
+
+// bf16 held in the low / high half of a 32-bit word, widened exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_round(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in 1..64, power of two). Every lane of
+// a group ends with the bit-identical sum: each step adds a lane's value to
+// its partner's, and float addition is commutative.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  if constexpr (N >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  if constexpr (N >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+  if constexpr (N >= 16) x += dpp_f32<0x140>(x); // row_mirror: lane i <-> 15 - i within 16
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,
+// at most 64 waves). `lds` needs NT/64 + 1 words. Returns the exclusive sum
+// and sets *total to the sum over the workgroup. Contains barriers: every
+// thread must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* lds, uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  uint32_t inc = wave_inclusive_scan(x, lane);
+  if (lane == kWave - 1) lds[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < NW ? lds[lane] : 0u;
+    uint32_t wi = wave_inclusive_scan(w, lane);
+    if (lane < NW) lds[lane] = wi - w;  // exclusive prefix of wave totals
+    if (lane == NW - 1) lds[NW] = wi;
+  }
+  __syncthreads();
+  uint32_t res = lds[wave] + inc - x;
+  *total = lds[NW];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace ppsa

@@ -1,0 +1,309 @@
+// C-ABI front end of the PPSA decode-step library: argument checks, split
+// planning, workspace carving and the per-layer dispatch of the decode step
+// (the three layer kinds of the TidalDecode review page, section 2 solution
+// overview and section 3 decode-step framework figure). Host code only;
+// it never allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "ppsa_internal.h"
+#include "../../include/ppsa.h"
+
+namespace ppsa {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kFullTargetGroups = 2048;   // workgroups a full layer is split into, about
+constexpr int kSparseTargetGroups = 1024; // same for a sparse layer
+constexpr int kMaxFullRows = 8192;
+constexpr int kMaxGridYZ = 65535;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int round_up(int64_t x, int g) { return (int)(ceil_div(x, g) * g); }
+
+struct Plan {
+  int full_rows = 0, full_splits = 0;
+  int sparse_rows = 0, sparse_splits = 0;
+  int max_splits = 0;
+  size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
+};
+
+size_t elem_bytes(int dtype) { return dtype == PPSA_BF16 ? 2 : 4; }
+
+// Scalar checks of the dims (no pointers).
+int check_dims(const ppsa_dims* d) {
+  if (!d) return PPSA_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq_len < 1 || d->head_dim < 1)
+    return PPSA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PPSA_ERR_INVALID_ARG;
+  if (!isfinite(d->scale)) return PPSA_ERR_INVALID_ARG;
+  if (d->dtype != PPSA_F32 && d->dtype != PPSA_BF16) return PPSA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PPSA_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > kMaxGroup) return PPSA_ERR_UNSUPPORTED;
+  if (d->batch > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ) return PPSA_ERR_UNSUPPORTED;
+  return PPSA_OK;
+}
+
+Plan make_plan(const ppsa_dims& d, int topk) {
+  Plan p;
+  const int granule = attn_rows_granule(d.dtype, d.head_dim);
+  const int64_t units = (int64_t)std::max(d.batch, 1) * d.num_kv_heads;
+  int64_t rows = ceil_div(units * d.max_seq_len, kFullTargetGroups);
+  p.full_rows = std::min(std::max(round_up(rows, granule), granule), round_up(kMaxFullRows, granule));
+  p.full_splits = (int)ceil_div(d.max_seq_len, p.full_rows);
+  if (topk > 0) {
+    rows = ceil_div(units * topk, kSparseTargetGroups);
+    const int cap = attn_max_sparse_rows() / granule * granule;
+    p.sparse_rows = std::min(std::max(round_up(rows, granule), granule), cap);
+    p.sparse_splits = (int)ceil_div(topk, p.sparse_rows);
+  }
+  p.max_splits = std::max(p.full_splits, p.sparse_splits);
+  const size_t heads = (size_t)std::max(d.batch, 0) * d.num_q_heads;
+  size_t off = 0;
+  p.off_m = off; off = align_up(off + heads * p.max_splits * sizeof(float));
+  p.off_l = off; off = align_up(off + heads * p.max_splits * sizeof(float));
+  p.off_o = off; off = align_up(off + heads * p.max_splits * d.head_dim * sizeof(float));
+  p.off_scores = off;
+  off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * d.max_seq_len * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+float eff_scale(const ppsa_dims& d) { return d.scale != 0.0f ? d.scale : 1.0f / sqrtf((float)d.head_dim); }
+
+struct Ctx {
+  const ppsa_dims* d;
+  Plan plan;
+  char* ws;
+  hipStream_t stream;
+};
+
+AttnArgs base_args(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.part_m = reinterpret_cast<float*>(c.ws + c.plan.off_m);
+  a.part_l = reinterpret_cast<float*>(c.ws + c.plan.off_l);
+  a.part_o = reinterpret_cast<float*>(c.ws + c.plan.off_o);
+  a.batch = c.d->batch;
+  a.q_heads = c.d->num_q_heads;
+  a.kv_heads = c.d->num_kv_heads;
+  a.group = c.d->num_q_heads / c.d->num_kv_heads;
+  a.max_len = c.d->max_seq_len;
+  a.scale = eff_scale(*c.d);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  return a;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? PPSA_OK : PPSA_ERR_HIP; }
+
+int run_combine(const Ctx& c, int splits, void* out) {
+  CombineArgs cb{};
+  cb.part_m = reinterpret_cast<const float*>(c.ws + c.plan.off_m);
+  cb.part_l = reinterpret_cast<const float*>(c.ws + c.plan.off_l);
+  cb.part_o = reinterpret_cast<const float*>(c.ws + c.plan.off_o);
+  cb.out = out;
+  cb.rows = c.d->batch * c.d->num_q_heads;
+  cb.splits = splits;
+  return finish(launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream));
+}
+
+int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx) {
+  SelectArgs s{};
+  s.scores = scores;
+  s.seq_lens = seq_lens;
+  s.idx = idx;
+  s.batch = c.d->batch;
+  s.kv_heads = c.d->num_kv_heads;
+  s.max_len = c.d->max_seq_len;
+  s.topk = topk;
+  return finish(launch_select(s, c.stream));
+}
+
+int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
+             int topk, float* scores, int32_t* idx) {
+  AttnArgs a = base_args(c, q, k, v, seq_lens);
+  a.splits = c.plan.full_splits;
+  a.rows_per_split = c.plan.full_rows;
+  const bool select = idx != nullptr;
+  if (select) a.scores = scores ? scores : reinterpret_cast<float*>(c.ws + c.plan.off_scores);
+  int rc = finish(launch_attn(a, select ? MODE_FULL_SCORES : MODE_FULL, c.d->dtype, c.d->head_dim, c.stream));
+  if (rc != PPSA_OK) return rc;
+  rc = run_combine(c, a.splits, out);
+  if (rc != PPSA_OK || !select) return rc;
+  return run_select(c, a.scores, seq_lens, topk, idx);
+}
+
+int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
+               const int32_t* idx, int topk, void* out) {
+  AttnArgs a = base_args(c, q, k, v, seq_lens);
+  a.idx = idx;
+  a.kslots = topk;
+  a.splits = c.plan.sparse_splits;
+  a.rows_per_split = c.plan.sparse_rows;
+  int rc = finish(launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream));
+  if (rc != PPSA_OK) return rc;
+  return run_combine(c, a.splits, out);
+}
+
+// Pointer and workspace checks common to the attention entry points.
+int check_tensors(const ppsa_dims* d, const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                  const void* out, const void* ws) {
+  if (!q || !k || !v || !seq_lens || !out || !ws) return PPSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(ws, 16) ||
+      !aligned(seq_lens, 4))
+    return PPSA_ERR_INVALID_ARG;
+  (void)d;
+  return PPSA_OK;
+}
+
+int check_topk(const ppsa_dims* d, int topk) {
+  return (topk >= 1 && topk <= d->max_seq_len) ? PPSA_OK : PPSA_ERR_INVALID_ARG;
+}
+
+}  // namespace
+}  // namespace ppsa
+
+using namespace ppsa;
+
+extern "C" {
+
+int ppsa_abi_version(void) { return PPSA_ABI_VERSION; }
+
+const char* ppsa_status_string(int status) {
+  switch (status) {
+    case PPSA_OK: return "ok";
+    case PPSA_ERR_INVALID_ARG: return "invalid argument";
+    case PPSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PPSA_ERR_WORKSPACE: return "workspace too small";
+    case PPSA_ERR_SCHEDULE: return "invalid decode schedule";
+    case PPSA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ppsa_workspace_bytes(const ppsa_dims* dims, int32_t topk) {
+  if (check_dims(dims) != PPSA_OK || topk < 0) return 0;
+  return make_plan(*dims, topk).total;
+}
+
+int ppsa_full_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if (dims->batch == 0) return PPSA_OK;
+  if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
+  Ctx c{dims, make_plan(*dims, 0), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return run_full(c, q, k_cache, v_cache, seq_lens, out, 0, nullptr, nullptr);
+}
+
+int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, int32_t topk, void* out, float* scores, int32_t* idx,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  if (dims->batch == 0) return PPSA_OK;
+  if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
+  if (!idx || !aligned(idx, 4) || (scores && !aligned(scores, 4))) return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return run_full(c, q, k_cache, v_cache, seq_lens, out, topk, scores, idx);
+}
+
+int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
+                     int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  if (dims->batch == 0) return PPSA_OK;
+  if (!scores || !seq_lens || !idx || !aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(idx, 4))
+    return PPSA_ERR_INVALID_ARG;
+  if (workspace_bytes > 0 && !workspace) return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  (void)hipGetLastError();
+  return run_select(c, scores, seq_lens, topk, idx);
+}
+
+int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const int32_t* idx, int32_t topk, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  if (dims->batch == 0) return PPSA_OK;
+  if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
+  if (!idx || !aligned(idx, 4)) return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out);
+}
+
+int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
+                     int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if (num_layers < 0 || (num_layers > 0 && !schedule)) return PPSA_ERR_INVALID_ARG;
+  int n_sel = 0;
+  for (int l = 0; l < num_layers; ++l) {
+    const int kind = schedule[l];
+    if (kind == PPSA_FULL_SELECT) ++n_sel;
+    else if (kind == PPSA_SPARSE) {
+      if (n_sel == 0) return PPSA_ERR_SCHEDULE;
+    } else if (kind != PPSA_FULL) {
+      return PPSA_ERR_SCHEDULE;
+    }
+  }
+  if (n_sel > 0 && (rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  if (dims->batch == 0 || num_layers == 0) return PPSA_OK;
+  if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
+  if (n_sel > 0 && (!idx || !aligned(idx, 4))) return PPSA_ERR_INVALID_ARG;
+  if (scores && !aligned(scores, 4)) return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0), static_cast<char*>(workspace),
+        static_cast<hipStream_t>(stream)};
+  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+
+  const size_t eb = elem_bytes(dims->dtype);
+  const size_t q_layer = (size_t)dims->batch * dims->num_q_heads * dims->head_dim * eb;
+  const size_t kv_layer = (size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len * dims->head_dim * eb;
+  const size_t idx_slot = (size_t)dims->batch * dims->num_kv_heads * (size_t)std::max(topk, 0);
+  const size_t score_slot = (size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len;
+  (void)hipGetLastError();
+  int sel = -1;
+  for (int l = 0; l < num_layers; ++l) {
+    const char* ql = static_cast<const char*>(q) + l * q_layer;
+    const char* kl = static_cast<const char*>(k_cache) + l * kv_layer;
+    const char* vl = static_cast<const char*>(v_cache) + l * kv_layer;
+    char* ol = static_cast<char*>(out) + l * q_layer;
+    switch (schedule[l]) {
+      case PPSA_FULL:
+        rc = run_full(c, ql, kl, vl, seq_lens, ol, 0, nullptr, nullptr);
+        break;
+      case PPSA_FULL_SELECT:
+        ++sel;
+        rc = run_full(c, ql, kl, vl, seq_lens, ol, topk, scores ? scores + sel * score_slot : nullptr,
+                      idx + sel * idx_slot);
+        break;
+      default:
+        rc = run_sparse(c, ql, kl, vl, seq_lens, idx + sel * idx_slot, topk, ol);
+        break;
+    }
+    if (rc != PPSA_OK) return rc;
+  }
+  return PPSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: exports, status text, workspace sizing and
+every argument-validation path (validation runs before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import position_persistent_sparse_amd as ppsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = ppsa.raw_library()
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced on failing paths
+ODD = ctypes.c_void_p(0x100004)       # misaligned for 16-byte operands
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ppsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ppsa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(LIB, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert ppsa.abi_version() == 1
+    assert ppsa.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert ppsa.status_string(code) not in ("ok", "unknown status")
+    assert ppsa.status_string(99) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(batch=2, q_heads=8, kv_heads=2, head_dim=128, max_seq_len=1000, dtype=ppsa.PPSA_BF16, scale=0.0)
+    base.update(kw)
+    return ppsa.make_dims(base["batch"], base["q_heads"], base["kv_heads"], base["head_dim"],
+                          base["max_seq_len"], base["dtype"], base["scale"])
+
+
+def full(d, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, ws=FAKE, ws_bytes=None):
+    wsb = ppsa.workspace_bytes(d, 0) if ws_bytes is None else ws_bytes
+    return LIB.ppsa_full_attn(ctypes.byref(d), q, k, v, lens, out, ws, wsb, None)
+
+
+def sparse(d, topk=16, idx=FAKE, ws_bytes=None, q=FAKE):
+    wsb = ppsa.workspace_bytes(d, topk) if ws_bytes is None else ws_bytes
+    return LIB.ppsa_sparse_attn(ctypes.byref(d), q, FAKE, FAKE, FAKE, idx, topk, FAKE, FAKE, wsb, None)
+
+
+def select(d, topk=16, idx=FAKE, scores=FAKE):
+    return LIB.ppsa_full_attn_select(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, topk, FAKE, scores, idx, FAKE,
+                                     ppsa.workspace_bytes(d, topk), None)
+
+
+def step(d, schedule, topk=16, idx=FAKE):
+    codes = ppsa.schedule_codes(schedule)
+    return LIB.ppsa_decode_step(ctypes.byref(d), len(schedule), codes, FAKE, FAKE, FAKE, FAKE, topk, FAKE, idx,
+                                None, FAKE, ppsa.workspace_bytes(d, topk), None)
+
+
+def test_workspace_bytes():
+    d = dims()
+    assert ppsa.workspace_bytes(d, 0) > 0
+    assert ppsa.workspace_bytes(d, 64) >= ppsa.workspace_bytes(d, 0)
+    assert ppsa.workspace_bytes(d, 64) % 256 == 0
+    assert ppsa.workspace_bytes(dims(head_dim=96), 0) == 0
+    assert ppsa.workspace_bytes(d, -1) == 0
+    # The workspace always holds a scores buffer for full+select without caller scores.
+    assert ppsa.workspace_bytes(d, 0) >= 2 * 2 * 1000 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), ppsa.PPSA_ERR_UNSUPPORTED),
+    (dict(head_dim=0), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(dtype=7), ppsa.PPSA_ERR_UNSUPPORTED),
+    (dict(q_heads=7), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(q_heads=34, kv_heads=2), ppsa.PPSA_ERR_UNSUPPORTED),
+    (dict(kv_heads=0), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(batch=-1), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(max_seq_len=0), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ppsa.PPSA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ppsa.PPSA_ERR_INVALID_ARG),
+])
+def test_bad_dims(kw, code):
+    d = dims(**kw)
+    assert full(d, ws_bytes=1 << 30) == code
+    assert sparse(d, ws_bytes=1 << 30) == code
+
+
+def test_null_and_misaligned_pointers():
+    d = dims()
+    for name in ("q", "k", "v", "lens", "out", "ws"):
+        assert full(d, **{name: None}) == ppsa.PPSA_ERR_INVALID_ARG, name
+    for name in ("q", "k", "v", "out", "ws"):
+        assert full(d, **{name: ODD}) == ppsa.PPSA_ERR_INVALID_ARG, name
+    assert sparse(d, idx=None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert select(d, idx=None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert select(d, scores=ctypes.c_void_p(0x100002)) == ppsa.PPSA_ERR_INVALID_ARG
+
+
+def test_topk_range():
+    d = dims()
+    assert sparse(d, topk=0) == ppsa.PPSA_ERR_INVALID_ARG
+    assert sparse(d, topk=1001) == ppsa.PPSA_ERR_INVALID_ARG
+    assert select(d, topk=0) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_select_topk(ctypes.byref(d), FAKE, FAKE, 1001, FAKE, None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG
+
+
+def test_workspace_too_small():
+    d = dims()
+    assert full(d, ws_bytes=ppsa.workspace_bytes(d, 0) - 1) == ppsa.PPSA_ERR_WORKSPACE
+    assert sparse(d, ws_bytes=ppsa.workspace_bytes(d, 16) - 256) == ppsa.PPSA_ERR_WORKSPACE
+
+
+def test_schedule_errors():
+    d = dims()
+    assert step(d, "FFS") == ppsa.PPSA_ERR_SCHEDULE
+    assert step(d, "S") == ppsa.PPSA_ERR_SCHEDULE
+    assert step(d, [0, 1, 7]) == ppsa.PPSA_ERR_SCHEDULE
+    assert step(d, "FFXS", topk=0) == ppsa.PPSA_ERR_INVALID_ARG
+    assert step(d, "FFXS", idx=None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_decode_step(ctypes.byref(d), 3, None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, FAKE,
+                                1 << 30, None) == ppsa.PPSA_ERR_INVALID_ARG
+
+
+def test_empty_batch_and_empty_schedule_are_noops():
+    d = dims(batch=0)
+    assert full(d, q=None, k=None, v=None, lens=None, out=None, ws=None, ws_bytes=0) == ppsa.PPSA_OK
+    assert LIB.ppsa_decode_step(ctypes.byref(dims()), 0, None, None, None, None, None, 0, None, None, None, None,
+                                0, None) == ppsa.PPSA_OK

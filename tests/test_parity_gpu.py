@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Reduced workloads keep every shape trait of the benchmark workloads (dtype,
+head_dim, group size, ragged lengths, two selection layers) at sizes the
+oracle finishes in seconds, spanning several split tiles and a ragged tail.
+The full-size test runs the benchmark workload in the launch configuration
+the benchmark times and checks sampled (batch row, KV head) units.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import position_persistent_sparse_amd as ppsa
+import synth
+from synth import torch_io
+
+from gpu_parity import check_layer, check_output
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+REDUCED = {
+    "tiny-f32": synth.WORKLOADS["tiny-f32"],
+    "llama2-7b-10k": synth.WORKLOADS["llama2-7b-10k"].with_(layers=9, q_heads=4, kv_heads=4, max_len=3001,
+                                                             topk=512, select_layers=(2, 7)),
+    "llama3-8b-gqa-32k": synth.WORKLOADS["llama3-8b-gqa-32k"].with_(layers=8, batch=2, q_heads=8, kv_heads=2,
+                                                                     max_len=6000, topk=1024,
+                                                                     select_layers=(2, 5)),
+    "llama2-7b-100k": synth.WORKLOADS["llama2-7b-100k"].with_(layers=6, q_heads=2, kv_heads=2, max_len=20000,
+                                                               topk=2048, select_layers=(2, 4)),
+    "llama3-70b-ragged-10k": synth.WORKLOADS["llama3-70b-ragged-10k"].with_(layers=6, batch=3, q_heads=16,
+                                                                             kv_heads=2, max_len=2100,
+                                                                             min_len=1500, topk=256,
+                                                                             select_layers=(2, 4)),
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_step(wl, gen, with_scores=True):
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    n_sel = wl.schedule().count("X")
+    scores = None
+    if with_scores:
+        scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32,
+                            device=DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores)
+    torch.cuda.synchronize()
+    return (torch_io.from_torch(out).astype(np.float64) if wl.dtype == "bf16" else out.cpu().numpy(),
+            idx.cpu().numpy() if idx is not None else None,
+            scores.cpu().numpy() if scores is not None else None, host)
+
+
+def widen_out(out, wl):
+    if wl.dtype == "bf16":
+        return (out.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return out.astype(np.float64)
+
+
+def check_step(wl, gen, name):
+    say(f"[parity] {name}: shape L={wl.layers} B={wl.batch} Hq={wl.q_heads} Hkv={wl.kv_heads} "
+        f"N={wl.max_len} k={wl.topk} {wl.dtype} lens={gen.seq_lens.tolist()}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    n_sel = wl.schedule().count("X")
+    scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32, device=DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores)
+    torch.cuda.synchronize()
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    sel = -1
+    worst = 0.0
+    for layer, kind in enumerate(wl.schedule()):
+        if kind == "X":
+            sel += 1
+        qh, kh, vh = host[layer]
+        worst = max(worst, check_layer(kind, wl, qh, kh, vh, gen.seq_lens, out_h[layer],
+                                       idx_h[sel] if sel >= 0 else None, sc_h[sel] if kind == "X" else None,
+                                       idx_h[sel] if sel >= 0 else None, f"{name} layer {layer} ({kind})"))
+    say(f"[parity] {name}: ok, max abs error {worst:.3e}")
+    return out, idx
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_decode_step_reduced(name):
+    wl = REDUCED[name]
+    check_step(wl, synth.Generator(wl), name)
+
+
+def test_padding_poison_and_determinism():
+    wl = REDUCED["llama3-70b-ragged-10k"]
+    gen = synth.Generator(wl, pad_mode=synth.PAD_NAN)
+    out1, idx1 = check_step(wl, gen, "ragged+NaN padding")
+    q, k, v, lens, _ = torch_io.upload(wl, gen, DEV)
+    out2, idx2 = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "outputs differ between two runs"
+    assert torch.equal(idx1, idx2)
+
+
+def test_edge_lengths_and_budget():
+    # One empty row, one single row, one row shorter than k, one at Nmax.
+    wl = synth.WORKLOADS["llama2-7b-10k"].with_(layers=4, batch=4, q_heads=4, kv_heads=2, max_len=700, topk=300,
+                                                select_layers=(2,))
+    gen = synth.Generator(wl, seq_lens=[0, 1, 200, 700], pad_mode=synth.PAD_NAN)
+    out, idx = check_step(wl, gen, "edge lengths")
+    o = out.float().cpu().numpy()
+    assert np.all(o[:, 0] == 0.0)
+    i = idx.cpu().numpy()
+    assert np.all(i[0, 0] == -1)
+    assert list(i[0, 1, 0, :2]) == [0, -1]
+    assert np.all(i[0, 2, :, :200] == np.arange(200)) and np.all(i[0, 2, :, 200:] == -1)
+
+
+@pytest.mark.parametrize("dtype,d,g", [("bf16", 64, 3), ("f32", 128, 2), ("bf16", 128, 16), ("f32", 64, 5)])
+def test_other_shapes(dtype, d, g):
+    wl = synth.Workload("shape", layers=5, batch=2, q_heads=2 * g, kv_heads=2, head_dim=d, max_len=777, topk=100,
+                        dtype=dtype, select_layers=(2, 3), seed=77, min_len=500)
+    check_step(wl, synth.Generator(wl), f"{dtype} d={d} g={g}")
+
+
+def test_q_zero_ties_select_prefix():
+    wl = synth.WORKLOADS["llama3-8b-gqa-32k"].with_(layers=3, batch=1, q_heads=8, kv_heads=2, max_len=1500,
+                                                    topk=333, select_layers=(2,))
+    gen = synth.Generator(wl)
+    q, k, v, lens, _ = torch_io.upload(wl, gen, DEV)
+    q.zero_()
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk)
+    torch.cuda.synchronize()
+    i = idx.cpu().numpy()
+    assert np.all(i[0] == np.arange(333)[None, None, :])
+    # q = 0: every weight equal, so each output is the mean of the live V rows.
+    vh = torch_io.from_torch(v[2])
+    mean = ((vh.astype(np.uint32) << 16).view(np.float32).astype(np.float64)).mean(axis=2)
+    got = widen_out(torch_io.from_torch(out[2]), wl)
+    for h in range(8):
+        check_output(got[0, h], mean[0, h // 4], "bf16", f"q=0 mean head {h}")
+
+
+def test_sparse_with_k_equal_n_matches_full():
+    wl = synth.WORKLOADS["llama3-8b-gqa-32k"].with_(layers=1, batch=2, q_heads=8, kv_heads=2, max_len=1200,
+                                                    topk=1200, select_layers=())
+    gen = synth.Generator(wl, seq_lens=[1200, 1111])
+    q, k, v, lens, _ = torch_io.upload(wl, gen, DEV)
+    full = ppsa.full_attn(q[0], k[0], v[0], lens)
+    idx = torch.arange(1200, dtype=torch.int32, device=DEV).flip(0).repeat(2, 2, 1).contiguous()
+    sp = ppsa.sparse_attn(q[0], k[0], v[0], lens, idx)
+    torch.cuda.synchronize()
+    a = widen_out(torch_io.from_torch(full), wl)
+    b = widen_out(torch_io.from_torch(sp), wl)
+    assert np.abs(a - b).max() <= 2 ** -8 * np.abs(a).max() + 1e-6
+
+
+def test_sparse_invalid_and_repeated_entries():
+    wl = synth.WORKLOADS["tiny-f32"].with_(layers=1, batch=1, q_heads=4, kv_heads=2, max_len=300, topk=40,
+                                           select_layers=())
+    gen = synth.Generator(wl, seq_lens=[250], pad_mode=synth.PAD_NAN)
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    rng = np.random.default_rng(4)
+    idx_h = rng.integers(-5, 300, size=(1, 2, 40)).astype(np.int32)
+    idx_h[0, 0, :6] = 17  # repeated entry
+    out = ppsa.sparse_attn(q[0], k[0], v[0], lens, torch.from_numpy(idx_h).to(DEV))
+    torch.cuda.synchronize()
+    qh, kh, vh = host[0]
+    scale = oracle.default_scale(wl.head_dim)
+    for h in range(2):
+        want = oracle.sparse_attention(qh[0, 2 * h:2 * h + 2].astype(np.float64), kh[0, h].astype(np.float64),
+                                       vh[0, h].astype(np.float64), idx_h[0, h], 250, scale)
+        check_output(out[0, 2 * h:2 * h + 2].cpu().numpy(), want, "f32", f"sparse invalid/repeat h={h}")
+
+
+def test_select_topk_on_crafted_scores():
+    B, H, N = 2, 3, 5000
+    rng = np.random.default_rng(8)
+    s = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 2.0], dtype=np.float32), size=(B, H, N))
+    s[1, 2] = rng.standard_normal(N).astype(np.float32)
+    s[0, 1, 4000:] = np.nan  # past seq_lens[0]: never read
+    lens = np.array([4000, 5000], dtype=np.int32)
+    for k in (1, 17, 1000, 3999, 4000, 4500):
+        idx = ppsa.select_topk(torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV), k)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                n = int(lens[b])
+                want = oracle.select_topk(s[b, h, :n], k)
+                assert sorted(got[b, h][got[b, h] >= 0].tolist()) == sorted(want[want >= 0].tolist()), (k, b, h)
+                assert np.all(got[b, h][min(k, n):] == -1)
+
+
+def test_full_size_bench_workload_sampled():
+    """The benchmark workload at full size, launch configuration as timed; sampled units checked."""
+    wl = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+    gen = synth.Generator(wl)
+    units = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    say(f"[parity] full-size {wl.name}: generating {wl.layers} layers")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV, keep_units=units)
+    n_sel = wl.schedule().count("X")
+    scores = torch.empty((n_sel, wl.batch, wl.kv_heads, wl.max_len), dtype=torch.float32, device=DEV)
+    ws = ppsa.alloc_workspace(ppsa.make_dims(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.max_len,
+                                             torch.bfloat16), wl.topk, DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores, workspace=ws)
+    torch.cuda.synchronize()
+    say("[parity] full-size: step done, checking sampled units")
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    g = wl.group
+    sel = -1
+    worst = 0.0
+    for layer, kind in enumerate(wl.schedule()):
+        if kind == "X":
+            sel += 1
+        for (b, h) in units:
+            qg, kh, vh = host[layer][(b, h)]
+            sub = wl.with_(batch=1, q_heads=g, kv_heads=1)
+            worst = max(worst, check_layer(
+                kind, sub, qg[None], kh[None, None], vh[None, None], gen.seq_lens[b:b + 1],
+                out_h[layer, b, h * g:(h + 1) * g][None], idx_h[sel, b:b + 1, h:h + 1] if sel >= 0 else None,
+                sc_h[sel, b:b + 1, h:h + 1] if kind == "X" else None,
+                idx_h[sel, b:b + 1, h:h + 1] if sel >= 0 else None, f"full-size layer {layer} unit {(b, h)}"))
+    say(f"[parity] full-size {wl.name}: ok, max abs error {worst:.3e}")
