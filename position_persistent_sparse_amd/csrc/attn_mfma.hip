@@ -1,0 +1,303 @@
+// Split attention pass on the matrix cores (gfx950, bf16, head_dim 128).
+//
+// Same contract as the vector-ALU pass (attn_valu.hip): per query head of a
+// KV group, softmax(q K^T * scale) V (TidalDecode review page, section 3,
+// PPSA paragraph, attention equation) over one split of rows -- cache rows
+// in order (full, full+scores) or the rows listed in idx (sparse) -- as a
+// partial for the merge pass (combine.hip), or as the output when the unit
+// has a single split.
+//
+// All query heads of a KV group share every K and V row, so the group's
+// logits for 16 rows are one 16x16 matrix product and the weighted V sum is
+// another; both go to the MFMA units, with up to 16 heads per group (heads
+// past the group size are zero columns). Each wave walks tiles of 32 rows
+// (two blocks of 16):
+//   S^T[row, head] = K[row, :] . q[head, :]
+//       v_mfma_f32_16x16x32_bf16, A = K (lane%16 = row, lane/16 picks 8 of
+//       each 32 dims), B = q (lane%16 = head); four products cover d = 128.
+//       Every lane loads 16-byte pieces of its row; the four lanes of a row
+//       group read 64 contiguous bytes.
+//   The result leaves lane (g = lane/16, n = lane%16) holding the logits of
+//   rows 4g..4g+3 for head n, which is exactly the A operand layout of
+//   v_mfma_f32_16x16x16_bf16 for P[head, row] over those 16 rows, so the
+//   softmax weights never leave the lane.
+//   O[head, dim] += P[head, :] . V[:, dim]
+//       B = V needs rows along the operand elements: lane (g, n) loads rows
+//       4g..4g+3 at dims 8n..8n+7 (16 lanes read whole 256-byte rows) and
+//       product t uses dim 8n+t of each, regrouped with v_perm_b32. The
+//       output column n of product t is dim 8n+t.
+// The running max is shared by the four lanes holding a head (two xor
+// shuffles per tile) and only moved when a tile exceeds it by more than
+// 2^8 ("lazy" rescaling: weights may reach 256, still exact in the float32
+// sums); the merge uses each partial's own max, so the result is the same
+// softmax. Weights are rounded to bf16 for the product and the normaliser
+// sums the rounded weights, so numerator and denominator match.
+#include <math.h>
+
+#include "attn_epilogue.h"
+#include "device_common.h"
+#include "ppsa_internal.h"
+#include "ppsa.h"
+
+namespace ppsa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kD = 128;
+constexpr int kTile = 32;
+constexpr int kRowsTrip = kTile * kWaves;
+constexpr int kMaxSparseRowsMfma = 2048;
+constexpr float kLazyLog2 = 8.0f;
+
+struct Tile {
+  uint4 k[2][4];   // [block][t]: K[row 16*blk + n][32t + 8g .. +8]
+  uint4 v[2][4];   // [block][i]: V[row 16*blk + 4g + i][8n .. +8]
+  bool valid[2][4];  // row 16*blk + 4g + i is live
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (uint32_t)bf16_round(lo) | ((uint32_t)bf16_round(hi) << 16);
+}
+
+template <int MODE>
+__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uint16_t* vb, int tslot, int slot0,
+                                          int slot_end, const int32_t* rows, int g, int n) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    {
+      const int slot = tslot + 16 * blk + n;
+      int row;
+      if constexpr (MODE == MODE_SPARSE) {
+        const int p = slot < slot_end ? rows[slot - slot0] : -1;
+        row = p >= 0 ? p : 0;
+      } else {
+        row = slot < slot_end ? slot : slot_end - 1;
+      }
+      const uint16_t* kp = kb + (size_t)row * kD + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t.k[blk][c] = *reinterpret_cast<const uint4*>(kp + 32 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = tslot + 16 * blk + 4 * g + i;
+      int row;
+      bool ok;
+      if constexpr (MODE == MODE_SPARSE) {
+        const int p = slot < slot_end ? rows[slot - slot0] : -1;
+        ok = p >= 0;
+        row = ok ? p : 0;
+      } else {
+        ok = slot < slot_end;
+        row = ok ? slot : slot_end - 1;
+      }
+      t.valid[blk][i] = ok;
+      t.v[blk][i] = *reinterpret_cast<const uint4*>(vb + (size_t)row * kD + 8 * n);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& u, int w) {
+  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
+  extern __shared__ float dyn[];  // [kWaves][group][kD] wave outputs, then staged sparse positions
+  __shared__ float sm_m[kWaves][kMaxGroup];
+  __shared__ float sm_l[kWaves][kMaxGroup];
+  const int group = a.group;
+  float* sm_o = dyn;
+  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + kWaves * group * kD);
+
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, n = lane % 16;
+
+  const int n_live = min(max(a.seq_lens[b], 0), a.max_len);
+  const size_t unit = (size_t)b * a.kv_heads + kv;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + unit * (size_t)a.max_len * kD;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + unit * (size_t)a.max_len * kD;
+  const int slot0 = split * a.rows_per_split;
+  int slot_end = MODE == MODE_SPARSE ? min(slot0 + a.rows_per_split, a.kslots)
+                                     : min(slot0 + a.rows_per_split, n_live);
+  if (n_live == 0) slot_end = slot0;
+
+  if constexpr (MODE == MODE_SPARSE) {
+    const int32_t* ip = a.idx + unit * (size_t)a.kslots;
+    for (int i = tid; i < slot_end - slot0; i += kThreads) {
+      const int p = ip[slot0 + i];
+      sm_rows[i] = (p >= 0 && p < n_live) ? p : -1;
+    }
+    __syncthreads();
+  }
+
+  // q fragments: head n, dims 32c + 8g .. +8 (zero for heads past the group).
+  bf16x8_t qf[4];
+  {
+    const int hn = n < group ? n : 0;  // address a real head; zero the padding heads after the load
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.q_heads + (size_t)kv * group + hn) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 w = *reinterpret_cast<const uint4*>(qp + 32 * c + 8 * g);
+      if (n >= group) w = make_uint4(0u, 0u, 0u, 0u);
+      qf[c] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  float4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY;  // per head n, shared by the four lanes of that head
+  float l_run = 0.0f;       // this lane's rows only
+
+  const int rows = slot_end - slot0;
+  const int ntiles = (rows + kTile - 1) / kTile;
+  auto process = [&](const Tile& cur, int ti) {
+    // Logits of rows 16*blk + 4g + j for head n.
+    float4_t s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[blk][c]), qf[c],
+                                                         s[blk], 0, 0, 0);
+    }
+    if constexpr (MODE == MODE_FULL_SCORES) {
+      const int tslot = slot0 + ti * kTile;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float tot = group_sum<16>(s[blk][j]);  // heads past the group contribute exact zeros
+          if (n == 0 && cur.valid[blk][j]) a.scores[unit * (size_t)a.max_len + tslot + 16 * blk + 4 * g + j] = tot * a.scale;
+        }
+    }
+    float x[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[blk][j] = cur.valid[blk][j] ? s[blk][j] * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[blk][j]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool need = tmax > m_run + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = need ? fmaxf(m_run, tmax) : m_run;
+      const float alpha = m_new == m_run ? 1.0f : exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * g + j);  // lane 4g+j holds head 4g+j
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t][j] *= aj;
+      }
+      m_run = m_new;
+    }
+    const float ms = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      uint32_t p01 = bf16_pair(exp2_fast(x[blk][0] - ms), exp2_fast(x[blk][1] - ms));
+      uint32_t p23 = bf16_pair(exp2_fast(x[blk][2] - ms), exp2_fast(x[blk][3] - ms));
+      l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+      const short4_t pa = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t d0 = __builtin_amdgcn_perm(word(cur.v[blk][1], t >> 1), word(cur.v[blk][0], t >> 1), sel);
+        const uint32_t d1 = __builtin_amdgcn_perm(word(cur.v[blk][3], t >> 1), word(cur.v[blk][2], t >> 1), sel);
+        const short4_t vbv = __builtin_bit_cast(short4_t, make_uint2(d0, d1));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vbv, acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  // One tile in flight per wave; occupancy (several waves per SIMD) hides the latency.
+  for (int ti = wave; ti < ntiles; ti += kWaves) {
+    Tile t;
+    load_tile<MODE>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
+    process(t, ti);
+  }
+
+  // Wave result: head n's max and normaliser; O rows are heads 4g + j, dims 8n + t.
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0 && n < group) {
+    sm_m[wave][n] = m_run;
+    sm_l[wave][n] = l_tot;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * g + j;
+    if (h < group) {
+      float* dst = sm_o + (wave * group + h) * kD + 8 * n;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dst[t] = acc[t][j];
+    }
+  }
+  __syncthreads();
+
+  const bool single = a.splits == 1;
+  for (int i = tid; i < group * kD; i += kThreads) {
+    const int h = i / kD, d = i % kD;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    const float ms = mx == -INFINITY ? 0.0f : mx;
+    float o = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = exp2_fast(sm_m[w][h] - ms);
+      o += sm_o[(w * group + h) * kD + d] * c;
+      lsum += sm_l[w][h] * c;
+    }
+    if (single) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)kv * group + h) * kD + d;
+      store_elem(op, lsum > 0.0f ? o / lsum : 0.0f);
+      continue;
+    }
+    const size_t row = part_row(a, b, kv, h, split);
+    a.part_o[row * kD + d] = o;
+    if (d == 0) {
+      a.part_m[row] = mx;
+      a.part_l[row] = lsum;
+    }
+  }
+}
+
+}  // namespace
+
+int attn_mfma_rows_granule() { return kRowsTrip; }
+int attn_mfma_max_sparse_rows() { return kMaxSparseRowsMfma; }
+
+bool attn_mfma_supported(int dtype, int head_dim, int group) {
+  return dtype == PPSA_BF16 && head_dim == kD && group >= 1 && group <= kMaxGroup;
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream) {
+  if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
+  if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRowsMfma) return hipErrorInvalidValue;
+  // Wave partial outputs, then the staged sparse positions.
+  size_t lds = (size_t)kWaves * a.group * kD * sizeof(float);
+  if (mode == MODE_SPARSE) lds += (size_t)a.rows_per_split * sizeof(int32_t);
+  dim3 grid(a.splits, a.kv_heads, a.batch), block(kThreads);
+  switch (mode) {
+    case MODE_FULL: attn_mfma_kernel<MODE_FULL><<<grid, block, lds, stream>>>(a); break;
+    case MODE_FULL_SCORES: attn_mfma_kernel<MODE_FULL_SCORES><<<grid, block, lds, stream>>>(a); break;
+    case MODE_SPARSE: attn_mfma_kernel<MODE_SPARSE><<<grid, block, lds, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ppsa

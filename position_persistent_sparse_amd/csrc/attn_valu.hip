@@ -13,14 +13,16 @@
 // wave-wide 16-byte load reads RPI = 64/LPR consecutive rows -- one
 // contiguous 1 KiB block when rows are consecutive. Each lane keeps an
 // independent softmax state per query head for its row slot; the slots of a
-// wave and then the four waves of the workgroup are merged at the end.
+// wave and then the four waves of the workgroup are merged at the end; the
+// splits of a unit are merged by the merge pass (combine.hip).
 // Every row's logit is reduced over its LPR lanes with DPP, so all lanes of
 // a row see the same bits.
 #include <math.h>
 
+#include "attn_epilogue.h"
 #include "device_common.h"
 #include "ppsa_internal.h"
-#include "../../include/ppsa.h"
+#include "ppsa.h"
 
 namespace ppsa {
 namespace {
@@ -211,7 +213,8 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Merge the waves and write this split's partial for each query head.
+  // Merge the waves: this split's result for each query head of the group.
+  const bool single = a.splits == 1;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i % D;
     if (h >= group) continue;
@@ -226,7 +229,12 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
       acc += sm_o[w][h][d] * c;
       lsum += sm_l[w][h] * c;
     }
-    const size_t row = ((size_t)b * a.q_heads + (size_t)kv * group + h) * a.splits + split;
+    if (single) {
+      T* o = reinterpret_cast<T*>(a.out) + ((size_t)b * a.q_heads + (size_t)kv * group + h) * D + d;
+      store_elem(o, lsum > 0.0f ? acc / lsum : 0.0f);
+      continue;
+    }
+    const size_t row = part_row(a, b, kv, h, split);
     a.part_o[row * D + d] = acc;
     if (d == 0) {
       a.part_m[row] = mx;

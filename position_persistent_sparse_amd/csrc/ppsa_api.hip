@@ -5,12 +5,13 @@
 // it never allocates, frees or synchronises.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
 
 #include "ppsa_internal.h"
-#include "../../include/ppsa.h"
+#include "ppsa.h"
 
 namespace ppsa {
 namespace {
@@ -18,8 +19,19 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kFullTargetGroups = 2048;   // workgroups a full layer is split into, about
 constexpr int kSparseTargetGroups = 1024; // same for a sparse layer
-constexpr int kMaxFullRows = 8192;
 constexpr int kMaxGridYZ = 65535;
+
+
+// Attention implementation: the matrix-core pass wherever it applies, unless
+// PPSA_ATTN_IMPL=valu selects the vector-ALU pass (both compute the same
+// result; the switch exists to compare them).
+bool use_mfma(const ppsa_dims& d) {
+  static const bool force_valu = [] {
+    const char* e = getenv("PPSA_ATTN_IMPL");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return !force_valu && attn_mfma_supported(d.dtype, d.head_dim, d.num_q_heads / d.num_kv_heads);
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -30,6 +42,8 @@ struct Plan {
   int sparse_rows = 0, sparse_splits = 0;
   int max_splits = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
+  bool ok = true;  // false: the budget needs more splits than one unit may have
+  bool mfma = false;
 };
 
 size_t elem_bytes(int dtype) { return dtype == PPSA_BF16 ? 2 : 4; }
@@ -50,15 +64,22 @@ int check_dims(const ppsa_dims* d) {
 
 Plan make_plan(const ppsa_dims& d, int topk) {
   Plan p;
-  const int granule = attn_rows_granule(d.dtype, d.head_dim);
+  p.mfma = use_mfma(d);
+  const int granule = p.mfma ? attn_mfma_rows_granule() : attn_rows_granule(d.dtype, d.head_dim);
   const int64_t units = (int64_t)std::max(d.batch, 1) * d.num_kv_heads;
   int64_t rows = ceil_div(units * d.max_seq_len, kFullTargetGroups);
-  p.full_rows = std::min(std::max(round_up(rows, granule), granule), round_up(kMaxFullRows, granule));
+  rows = std::max<int64_t>(rows, ceil_div(d.max_seq_len, kMaxSplitsPerUnit));
+  p.full_rows = std::max(round_up(rows, granule), granule);
   p.full_splits = (int)ceil_div(d.max_seq_len, p.full_rows);
   if (topk > 0) {
     rows = ceil_div(units * topk, kSparseTargetGroups);
-    const int cap = attn_max_sparse_rows() / granule * granule;
-    p.sparse_rows = std::min(std::max(round_up(rows, granule), granule), cap);
+    rows = std::max<int64_t>(rows, ceil_div(topk, kMaxSplitsPerUnit));
+    const int cap = (p.mfma ? attn_mfma_max_sparse_rows() : attn_max_sparse_rows()) / granule * granule;
+    p.sparse_rows = std::max(round_up(rows, granule), granule);
+    if (p.sparse_rows > cap) {
+      p.ok = false;
+      p.sparse_rows = cap;
+    }
     p.sparse_splits = (int)ceil_div(topk, p.sparse_rows);
   }
   p.max_splits = std::max(p.full_splits, p.sparse_splits);
@@ -84,8 +105,10 @@ struct Ctx {
   hipStream_t stream;
 };
 
-AttnArgs base_args(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens) {
+AttnArgs base_args(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                   void* out) {
   AttnArgs a{};
+  a.out = out;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -105,7 +128,9 @@ AttnArgs base_args(const Ctx& c, const void* q, const void* k, const void* v, co
 
 int finish(hipError_t e) { return e == hipSuccess ? PPSA_OK : PPSA_ERR_HIP; }
 
+// Merge pass after a multi-split attention launch (a single split writes out itself).
 int run_combine(const Ctx& c, int splits, void* out) {
+  if (splits <= 1) return PPSA_OK;
   CombineArgs cb{};
   cb.part_m = reinterpret_cast<const float*>(c.ws + c.plan.off_m);
   cb.part_l = reinterpret_cast<const float*>(c.ws + c.plan.off_l);
@@ -130,28 +155,29 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
 
 int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
              int topk, float* scores, int32_t* idx) {
-  AttnArgs a = base_args(c, q, k, v, seq_lens);
+  AttnArgs a = base_args(c, q, k, v, seq_lens, out);
   a.splits = c.plan.full_splits;
   a.rows_per_split = c.plan.full_rows;
   const bool select = idx != nullptr;
   if (select) a.scores = scores ? scores : reinterpret_cast<float*>(c.ws + c.plan.off_scores);
-  int rc = finish(launch_attn(a, select ? MODE_FULL_SCORES : MODE_FULL, c.d->dtype, c.d->head_dim, c.stream));
-  if (rc != PPSA_OK) return rc;
-  rc = run_combine(c, a.splits, out);
+  const int mode = select ? MODE_FULL_SCORES : MODE_FULL;
+  int rc = finish(c.plan.mfma ? launch_attn_mfma(a, mode, c.stream)
+                              : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream));
+  if (rc == PPSA_OK) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
   return run_select(c, a.scores, seq_lens, topk, idx);
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
                const int32_t* idx, int topk, void* out) {
-  AttnArgs a = base_args(c, q, k, v, seq_lens);
+  AttnArgs a = base_args(c, q, k, v, seq_lens, out);
   a.idx = idx;
   a.kslots = topk;
   a.splits = c.plan.sparse_splits;
   a.rows_per_split = c.plan.sparse_rows;
-  int rc = finish(launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream));
-  if (rc != PPSA_OK) return rc;
-  return run_combine(c, a.splits, out);
+  const int rc = finish(c.plan.mfma ? launch_attn_mfma(a, MODE_SPARSE, c.stream)
+                                    : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream));
+  return rc == PPSA_OK ? run_combine(c, a.splits, out) : rc;
 }
 
 // Pointer and workspace checks common to the attention entry points.
@@ -246,6 +272,7 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
   if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
   if (!idx || !aligned(idx, 4)) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (!c.plan.ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
   return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out);
@@ -274,6 +301,7 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
   if (scores && !aligned(scores, 4)) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0), static_cast<char*>(workspace),
         static_cast<hipStream_t>(stream)};
+  if (!c.plan.ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
 
   const size_t eb = elem_bytes(dims->dtype);

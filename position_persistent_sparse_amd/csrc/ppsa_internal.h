@@ -13,10 +13,12 @@ enum AttnMode : int { MODE_FULL = 0, MODE_FULL_SCORES = 1, MODE_SPARSE = 2 };
 // One launch of the split attention pass. Every pointer is a device pointer.
 // The grid is (splits, Hkv, B); split s of unit (b, kv) covers slots
 // [s*rows_per_split, (s+1)*rows_per_split) -- cache rows in full mode,
-// entries of idx[b, kv, :] in sparse mode -- and writes one partial
+// entries of idx[b, kv, :] in sparse mode. With one split the workgroup
+// writes out[b, hq, :] itself; otherwise each split leaves a partial
 // (m, l, o) per query head of the group:
 //   m = max over its rows of the logit in log2 units (-inf if none),
-//   l = sum 2^(logit - m), o[:] = sum 2^(logit - m) V[row, :].
+//   l = sum 2^(logit - m), o[:] = sum 2^(logit - m) V[row, :],
+// and the merge pass (launch_combine) turns them into out.
 struct AttnArgs {
   const void* q;            // [B, Hq, D]
   const void* k;            // [B, Hkv, Nmax, D]
@@ -24,6 +26,7 @@ struct AttnArgs {
   const int32_t* seq_lens;  // [B]
   const int32_t* idx;       // sparse: [B, Hkv, kslots]
   float* scores;            // full+scores: [B, Hkv, Nmax]
+  void* out;                // [B, Hq, D], dtype of the cache
   float* part_m;            // [B, Hq, splits]
   float* part_l;            // [B, Hq, splits]
   float* part_o;            // [B, Hq, splits, D]
@@ -36,12 +39,12 @@ struct AttnArgs {
 
 // Merge the partials of every (b, hq) into out[b, hq, :] (dtype of the cache).
 struct CombineArgs {
-  const float* part_m;
-  const float* part_l;
-  const float* part_o;
-  void* out;                // [B, Hq, D]
+  const float* part_m;      // [rows, splits]
+  const float* part_l;      // [rows, splits]
+  const float* part_o;      // [rows, splits, D]
+  void* out;                // [rows, D]
   int32_t rows;             // B * Hq
-  int32_t splits;
+  int32_t splits;           // 1 .. kMaxSplitsPerUnit
 };
 
 struct SelectArgs {
@@ -51,12 +54,21 @@ struct SelectArgs {
   int32_t batch, kv_heads, max_len, topk;
 };
 
-// Rows one attention workgroup covers per loop trip (split sizes are multiples).
+// Vector-ALU attention pass (any supported dtype / head_dim / group).
+// Rows one workgroup covers per loop trip, and the largest sparse split
+// (idx entries staged in LDS).
 int attn_rows_granule(int dtype, int head_dim);
-// Largest split (in idx entries) the sparse mode stages in LDS.
 int attn_max_sparse_rows();
+
+// Matrix-core attention pass (bf16, head_dim 128, group <= 16).
+bool attn_mfma_supported(int dtype, int head_dim, int group);
+int attn_mfma_rows_granule();
+int attn_mfma_max_sparse_rows();
+hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream);
 // Largest group size the attention kernels take.
 constexpr int kMaxGroup = 16;
+// Most splits one unit may be cut into (the merge pass keeps one weight per split in LDS).
+constexpr int kMaxSplitsPerUnit = 256;
 
 hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);

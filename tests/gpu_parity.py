@@ -15,18 +15,32 @@ def bf16_ulp(x):
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def check_output(got, want, dtype, where):
+def check_output(got, want, dtype, where, abs_weighted=None):
+    """Official gate: max abs error <= TOL[dtype].
+
+    bf16 also gets a per-element bound derived from the arithmetic: the
+    softmax weights may be rounded to bf16 (relative error <= 2^-8 each,
+    so each normalised weight moves by <= ~2^-7 of itself), which moves an
+    output by at most 2^-7 * sum_j w_j |V_j| (`abs_weighted`, the attention
+    of |V|); the output is then rounded to bf16 (<= one spacing), plus 1e-5
+    for float32 accumulation.
+    """
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - want)
     assert np.all(np.isfinite(got)), f"{where}: non-finite output"
     worst = float(err.max()) if err.size else 0.0
     assert worst <= TOL[dtype], f"{where}: max abs error {worst:.3e} > {TOL[dtype]}"
-    if dtype == "bf16":
-        # Stricter internal bound: one bf16 spacing of the exact value plus 1e-4.
-        bound = bf16_ulp(want) + 1e-4
+    if dtype == "bf16" and abs_weighted is not None:
+        bound = 2.0 ** -7 * 1.01 * abs_weighted + bf16_ulp(want) + 1e-5
         bad = int(np.sum(err > bound))
-        assert bad == 0, f"{where}: {bad} elements beyond one bf16 spacing (+1e-4)"
+        assert bad == 0, f"{where}: {bad} elements beyond the weight-rounding bound (worst excess " \
+                         f"{float(np.max(err - bound)):.3e})"
     return worst
+
+
+def abs_storage(x, dtype):
+    """|x| in storage form: clear the bf16 sign bit, or np.abs for float32."""
+    return (np.asarray(x) & np.uint16(0x7FFF)) if dtype == "bf16" else np.abs(x)
 
 
 def check_layer(kind, wl, q, K, V, seq_lens, gpu_out, gpu_idx, gpu_scores, selection, where):
@@ -39,7 +53,11 @@ def check_layer(kind, wl, q, K, V, seq_lens, gpu_out, gpu_idx, gpu_scores, selec
     scale = oracle.default_scale(wl.head_dim)
     want, _, oscores = oracle.decode_layer(kind, q, K, V, seq_lens, wl.group, wl.topk, scale, wl.dtype,
                                            selection if kind == "S" else None)
-    err = check_output(gpu_out, want, wl.dtype, where)
+    absw = None
+    if wl.dtype == "bf16":
+        absw, _, _ = oracle.decode_layer(kind, q, K, abs_storage(V, wl.dtype), seq_lens, wl.group, wl.topk, scale,
+                                         wl.dtype, selection if kind == "S" else None)
+    err = check_output(gpu_out, want, wl.dtype, where, absw)
     if kind == "X":
         for b in range(q.shape[0]):
             n = min(max(int(seq_lens[b]), 0), K.shape[2])
