@@ -40,14 +40,28 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32_or_zero(uint32_t x) {
+  // Lanes whose source is outside the row, or whose row is masked off, read 0.
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, on the VALU through DPP:
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+// row 0 (2) is added to row 1 (3) and the last lane of row 1 to rows 2, 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_u32_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_u32_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_u32_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_u32_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_u32_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_u32_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
   return x;
+}
+
+// Sum over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(x), kWave - 1);
 }
 
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,
@@ -58,12 +72,12 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* lds, uint32_t* total) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  uint32_t inc = wave_inclusive_scan(x, lane);
+  uint32_t inc = wave_inclusive_scan(x);
   if (lane == kWave - 1) lds[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     uint32_t w = lane < NW ? lds[lane] : 0u;
-    uint32_t wi = wave_inclusive_scan(w, lane);
+    uint32_t wi = wave_inclusive_scan(w);
     if (lane < NW) lds[lane] = wi - w;  // exclusive prefix of wave totals
     if (lane == NW - 1) lds[NW] = wi;
   }

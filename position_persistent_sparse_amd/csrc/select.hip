@@ -5,17 +5,27 @@
 // with the highest attention score. Scores are float32; equal scores go to
 // the lower position. Output is the selected positions in ascending order.
 //
-// Method: one 1024-thread workgroup per unit. Positions are read in rounds
-// of 4096: in round r thread t holds positions 4096r + 4t .. 4096r + 4t + 3
-// (one 16-byte load when the row is 16-byte aligned). Each score maps to an
-// order-preserving 32-bit key (-0.0 folded onto +0.0), so ranking floats is
-// ranking unsigned integers. An MSB-first radix select over digits of 11,
-// 11 and 10 bits (histograms in LDS) finds the exact key T of the k-th
-// largest score and how many keys equal to T are still needed. The output
-// pass walks the rounds in position order; one workgroup prefix sum per
-// round over packed (count > T, count == T) gives each thread its first
-// output slot. Rows of up to kCachedRounds rounds keep their keys in
-// registers; longer rows are re-read from memory on each pass.
+// One 1024-thread workgroup per unit; the work is bound by instruction issue
+// on that one CU, so every step keeps the per-score work to a few
+// instructions and avoids per-score branches. Positions are taken in
+// super-rounds of up to 32768: in super-round r thread t owns per_r
+// contiguous positions (per_r = ceil(n_r / 1024) <= 32, loaded 16 bytes at a
+// time when aligned), so position order is (super-round, thread, bit). Each score maps to an
+// order-preserving 32-bit key (-0.0 folded onto +0.0): ranking floats is
+// ranking unsigned integers.
+//  1. Radix digit 1 (key bits 31..21) over all keys: an LDS histogram and a
+//     workgroup scan of the bins from the top give the bin holding the k-th
+//     largest key and how many keys lie above it.
+//  2. The keys of that bin (the candidates) are copied to LDS; digits 2
+//     (bits 20..10) and 3 (bits 9..0) are resolved over the candidates only,
+//     giving the exact key T of the k-th largest score and how many keys
+//     equal to T are still to take (lowest positions first). If the bin does
+//     not fit in LDS (heavily tied scores), digits 2 and 3 run over all keys.
+//  3. Each thread builds bit masks of its keys > T and == T; one workgroup
+//     prefix sum of the packed counts gives its first output slot, and it
+//     writes its kept positions in order by walking the set bits.
+// Rows of one super-round keep their keys in registers through all steps;
+// longer rows reload their super-rounds in each step.
 #include <math.h>
 
 #include "device_common.h"
@@ -25,9 +35,11 @@ namespace ppsa {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kPerRound = 4 * kThreads;
-constexpr int kCachedRounds = 8;
-constexpr int kMaxBins = 2048;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kCached = 32;                    // positions per thread and super-round
+constexpr int kPerSuper = kCached * kThreads;  // positions per super-round
+constexpr int kBins = 2048;
+constexpr int kMaxCand = 8192;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -35,29 +47,45 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-struct Pass {
-  int shift, bins;
-};
-__device__ __forceinline__ Pass pass_of(int p) {
-  return p == 0 ? Pass{21, 2048} : (p == 1 ? Pass{10, 2048} : Pass{0, 1024});
+// With the histogram of one digit complete: finds the digit (walking bins
+// from the top) at which the running count reaches `remaining`, and
+// publishes it with the count of keys above it. Barriers inside.
+template <int BINS>
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining, uint32_t* scan_lds,
+                                           uint32_t* digit, uint32_t* above_out) {
+  constexpr int per = BINS / kThreads;  // 2 or 1
+  const int tid = threadIdx.x;
+  const int top = BINS - 1 - tid * per;
+  const uint32_t c0 = hist[top], c1 = per == 2 ? hist[top - 1] : 0u;
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan<kThreads>(c0 + c1, scan_lds, &total);
+  if (above < remaining && remaining <= above + c0) {
+    *digit = (uint32_t)top;
+    *above_out = above;
+  } else if (per == 2 && above + c0 < remaining && remaining <= above + c0 + c1) {
+    *digit = (uint32_t)(top - 1);
+    *above_out = above + c0;
+  }
+  __syncthreads();
 }
 
-// Keys of positions p0..p0+3 (key 0 past n; callers mask with p < n).
-__device__ __forceinline__ void load_keys(const float* s, int p0, int n, bool vec, uint32_t (&k)[4]) {
-  if (vec && p0 + 3 < n) {
-    const float4 f = *reinterpret_cast<const float4*>(s + p0);
-    k[0] = order_key(f.x); k[1] = order_key(f.y); k[2] = order_key(f.z); k[3] = order_key(f.w);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k[e] = p0 + e < n ? order_key(s[p0 + e]) : 0u;
+// The lowest `count` set bits of m.
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
+  uint32_t r = 0u;
+  for (uint32_t i = 0; i < count && m; ++i) {
+    const uint32_t low = m & (0u - m);
+    r |= low;
+    m ^= low;
   }
+  return r;
 }
 
 template <bool CACHED>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
-  __shared__ uint32_t hist[kMaxBins];
-  __shared__ uint32_t scan_lds[kThreads / kWave + 1];
-  __shared__ uint32_t found_digit, found_above;
+  __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
+  __shared__ uint32_t scan_lds[kWaves + 1];
+  __shared__ uint32_t cand[kMaxCand];
+  __shared__ uint32_t s_digit, s_above, s_ncand;
 
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int b = unit / a.kv_heads;
@@ -71,92 +99,138 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
     return;
   }
 
-  // Every row starts 16-byte aligned when the base is and rows hold a multiple of 4 scores.
-  const bool vec = (a.max_len % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) % 16) == 0;
-  const int rounds = (n + kPerRound - 1) / kPerRound;
-  uint32_t keys[CACHED ? kCachedRounds : 1][4];
-  if constexpr (CACHED) {
+  // Rows start 16-byte aligned when the base is and hold a multiple of 4 scores.
+  const bool aligned = (a.max_len % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) % 16) == 0;
+  const int n_sr = (n + kPerSuper - 1) / kPerSuper;
+  // Super-round r spans n_r positions; thread t owns per_r = ceil(n_r / 1024) of them from
+  // p0(r, t) = 32768 r + t per_r. Loads this thread's keys (0 past its live ones) and the
+  // mask of the live ones.
+  struct Span {
+    int p0, per;
+    uint32_t live;
+  };
+  auto load_sr = [&](int r, auto& k) -> Span {
+    const int n_r = min(kPerSuper, n - r * kPerSuper);
+    const int per = (n_r + kThreads - 1) / kThreads;
+    const int p0 = r * kPerSuper + tid * per;
+    const int cnt = max(0, min(per, r * kPerSuper + n_r - p0));
+    const uint32_t live = cnt >= kCached ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+    if (aligned && (per % 4) == 0 && cnt == per) {
 #pragma unroll
-    for (int r = 0; r < kCachedRounds; ++r)
-      if (r < rounds) load_keys(s, r * kPerRound + 4 * tid, n, vec, keys[r]);
-  }
-  // Calls fn(round, keys of this thread's 4 positions in that round) for every
-  // round in order; the round count is the same in every thread.
-  auto for_each_round = [&](auto&& fn) {
-    if constexpr (CACHED) {
-#pragma unroll
-      for (int rr = 0; rr < kCachedRounds; ++rr)
-        if (rr < rounds) fn(rr, keys[rr]);
+      for (int j = 0; j < kCached / 4; ++j)
+        if (4 * j < per) {
+          const float4 f = *reinterpret_cast<const float4*>(s + p0 + 4 * j);
+          k[4 * j] = order_key(f.x);
+          k[4 * j + 1] = order_key(f.y);
+          k[4 * j + 2] = order_key(f.z);
+          k[4 * j + 3] = order_key(f.w);
+        }
     } else {
-      for (int rr = 0; rr < rounds; ++rr) {
-        uint32_t kk[4];
-        load_keys(s, rr * kPerRound + 4 * tid, n, vec, kk);
-        fn(rr, kk);
+#pragma unroll
+      for (int i = 0; i < kCached; ++i)
+        if (i < per) k[i] = i < cnt ? order_key(s[p0 + i]) : 0u;
+    }
+    return Span{p0, per, live};
+  };
+  uint32_t keys[CACHED ? kCached : 1];
+  Span span{0, 0, 0u};
+  if constexpr (CACHED) span = load_sr(0, keys);
+  // fn(keys, span) for every super-round in order.
+  auto for_sr = [&](auto&& fn) {
+    if constexpr (CACHED) {
+      fn(keys, span);
+    } else {
+      for (int r = 0; r < n_sr; ++r) {
+        uint32_t kk[kCached];  // per trip, so it stays in registers
+        const Span sp = load_sr(r, kk);
+        fn(kk, sp);
       }
     }
   };
 
-  uint32_t prefix = 0u, mask = 0u;
-  uint32_t remaining = (uint32_t)k_eff;  // still to take among keys matching the prefix
-#pragma unroll 1
-  for (int p = 0; p < 3; ++p) {
-    const Pass ps = pass_of(p);
-    for (int i = tid; i < ps.bins; i += kThreads) hist[i] = 0u;
-    __syncthreads();
-    for_each_round([&](int rr, const uint32_t(&kk)[4]) {
-      const int p0 = rr * kPerRound + 4 * tid;
+  // 1. Digit 1 over all keys (padding slots count into the spare bin).
+  for (int i = tid; i <= kBins; i += kThreads) hist[i] = 0u;
+  if (tid == 0) s_ncand = 0u;
+  __syncthreads();
+  for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (p0 + e < n && (kk[e] & mask) == prefix) atomicAdd(&hist[(kk[e] >> ps.shift) & (ps.bins - 1)], 1u);
+    for (int i = 0; i < kCached; ++i)
+      if (i < sp.per) atomicAdd(&hist[((sp.live >> i) & 1u) ? (k[i] >> 21) : (uint32_t)kBins], 1u);
+  });
+  __syncthreads();
+  uint32_t remaining = (uint32_t)k_eff;
+  find_digit<kBins>(hist, remaining, scan_lds, &s_digit, &s_above);
+  uint32_t prefix = s_digit << 21;
+  uint32_t mask = 0xFFE00000u;
+  remaining -= s_above;
+  const uint32_t n_cand = hist[s_digit];
+  const bool use_cand = n_cand <= (uint32_t)kMaxCand;
+  __syncthreads();
+
+  // 2. Digits 2 and 3, over the candidates (or over all keys if they do not fit).
+  if (use_cand)
+    for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
+#pragma unroll
+      for (int i = 0; i < kCached; ++i)
+        if (i < sp.per && ((sp.live >> i) & 1u) && (k[i] & mask) == prefix) cand[atomicAdd(&s_ncand, 1u)] = k[i];
     });
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
+    for (int i = tid; i <= kBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
-    // Bins in descending digit order, bins/kThreads per thread; the exclusive
-    // scan gives the number of keys with a larger digit.
-    const int per_bin = ps.bins / kThreads;  // 2 or 1
-    const int top = ps.bins - 1 - tid * per_bin;
-    const uint32_t c[2] = {hist[top], per_bin == 2 ? hist[top - 1] : 0u};
-    uint32_t total;
-    uint32_t above = block_exclusive_scan<kThreads>(c[0] + c[1], scan_lds, &total);
-    for (int j = 0; j < per_bin; ++j) {
-      if (above < remaining && remaining <= above + c[j]) {
-        found_digit = (uint32_t)(top - j);
-        found_above = above;
+    if (use_cand) {
+      for (uint32_t i = tid; i < n_cand; i += kThreads) {
+        const uint32_t key = cand[i];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
       }
-      above += c[j];
+    } else {
+      for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
+#pragma unroll
+        for (int i = 0; i < kCached; ++i)
+          if (i < sp.per && ((sp.live >> i) & 1u) && (k[i] & mask) == prefix)
+            atomicAdd(&hist[(k[i] >> shift) & dmask], 1u);
+      });
     }
     __syncthreads();
-    prefix |= found_digit << ps.shift;
-    mask |= (uint32_t)(ps.bins - 1) << ps.shift;
-    remaining -= found_above;
+    if (pass == 0) find_digit<2048>(hist, remaining, scan_lds, &s_digit, &s_above);
+    else find_digit<1024>(hist, remaining, scan_lds, &s_digit, &s_above);
+    prefix |= s_digit << shift;
+    mask |= dmask << shift;
+    remaining -= s_above;
     __syncthreads();
   }
   const uint32_t thresh = prefix;
   const uint32_t needed_eq = remaining;  // >= 1 keys equal to thresh, lowest positions first
 
-  uint32_t written = 0u, eq_seen = 0u;
-  for_each_round([&](int rr, const uint32_t(&kk)[4]) {
-    const int p0 = rr * kPerRound + 4 * tid;
-    uint32_t gt = 0u, eq = 0u;
+  // 3. Output in position order (super-round, thread, bit).
+  uint32_t gt_seen = 0u, eq_seen = 0u;  // over earlier super-rounds
+  for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
+    uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p0 + e < n) {
-        gt += kk[e] > thresh;
-        eq += kk[e] == thresh;
+    for (int i = 0; i < kCached; ++i)
+      if (i < sp.per) {
+        gtm |= (uint32_t)(k[i] > thresh) << i;
+        eqm |= (uint32_t)(k[i] == thresh) << i;
       }
-    uint32_t total;
-    const uint32_t before = block_exclusive_scan<kThreads>(gt | (eq << 16), scan_lds, &total);
-    const uint32_t room = needed_eq > eq_seen ? needed_eq - eq_seen : 0u;  // equal keys still to take
-    uint32_t eq_before = before >> 16;
-    uint32_t slot = written + (before & 0xffffu) + min(eq_before, room);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p0 + e < n) {
-        const bool take = kk[e] > thresh || (kk[e] == thresh && eq_before < room);
-        if (kk[e] == thresh) ++eq_before;
-        if (take) out[slot++] = p0 + e;
-      }
-    written += (total & 0xffffu) + min(total >> 16, room);
-    eq_seen += total >> 16;
+    gtm &= sp.live;
+    eqm &= sp.live;
+    const uint32_t n_gt = __popc(gtm), n_eq = __popc(eqm);
+    uint32_t tot_gt, tot_eq;
+    const uint32_t gt_before = gt_seen + block_exclusive_scan<kThreads>(n_gt, scan_lds, &tot_gt);
+    const uint32_t eq_before = eq_seen + block_exclusive_scan<kThreads>(n_eq, scan_lds, &tot_eq);
+    // Saturating forms only: hipcc 7.2 turned a guarded `needed - before` feeding min() into an
+    // unconditional one assumed not to wrap, which dropped the clamp on the slot below.
+    const uint32_t room = max(needed_eq, eq_before) - eq_before;  // keys == T this thread may take
+    uint32_t take = gtm | lowest_bits(eqm, min(room, n_eq));
+    uint32_t slot = gt_before + (needed_eq - room);              // + min(eq_before, needed_eq)
+    while (take) {
+      out[slot++] = sp.p0 + __ffs(take) - 1;
+      take &= take - 1u;
+    }
+    gt_seen += tot_gt;
+    eq_seen += tot_eq;
   });
 }
 
@@ -165,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
   const dim3 grid(a.batch * a.kv_heads), block(kThreads);
-  if (a.max_len <= kCachedRounds * kPerRound) select_topk_kernel<true><<<grid, block, 0, stream>>>(a);
+  if (a.max_len <= kPerSuper) select_topk_kernel<true><<<grid, block, 0, stream>>>(a);
   else select_topk_kernel<false><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -24,13 +24,14 @@ def from_torch(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def upload(wl, gen, device, keep_layers=None, keep_units=None, progress=None):
+def upload(wl, gen, device, keep_layers=None, keep_units=None, progress=None, visit=None):
     """Generate every layer and copy it to `device`.
 
     Returns (q [L,B,Hq,d], k, v [L,B,Hkv,N,d], seq_lens [B] int32, host) where
     host[layer] = (q, K, V) numpy arrays for layers in keep_layers (all if
     None), restricted to the (b, h) pairs in keep_units when given (as dicts
-    {(b, h): (q_group, K_unit, V_unit)}).
+    {(b, h): (q_group, K_unit, V_unit)}). visit(layer, q, K, V), if given,
+    sees each layer's host arrays before their buffers are reused.
     """
     L, B, Hq, Hkv, N, d = wl.layers, wl.batch, wl.q_heads, wl.kv_heads, wl.max_len, wl.head_dim
     dt = torch_dtype(wl)
@@ -52,6 +53,8 @@ def upload(wl, gen, device, keep_layers=None, keep_units=None, progress=None):
                 g = wl.group
                 host[layer] = {(b, h): (qh[b, h * g:(h + 1) * g].copy(), kb[b, h].copy(), vb[b, h].copy())
                                for (b, h) in keep_units}
+        if visit:
+            visit(layer, qh, kb, vb)
         if progress:
             progress(layer)
     lens = torch.from_numpy(gen.seq_lens.copy()).to(device)

@@ -44,20 +44,6 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_step(wl, gen, with_scores=True):
-    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
-    n_sel = wl.schedule().count("X")
-    scores = None
-    if with_scores:
-        scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32,
-                            device=DEV)
-    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores)
-    torch.cuda.synchronize()
-    return (torch_io.from_torch(out).astype(np.float64) if wl.dtype == "bf16" else out.cpu().numpy(),
-            idx.cpu().numpy() if idx is not None else None,
-            scores.cpu().numpy() if scores is not None else None, host)
-
-
 def widen_out(out, wl):
     if wl.dtype == "bf16":
         return (out.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -192,6 +178,34 @@ def test_select_topk_on_crafted_scores():
                 want = oracle.select_topk(s[b, h, :n], k)
                 assert sorted(got[b, h][got[b, h] >= 0].tolist()) == sorted(want[want >= 0].tolist()), (k, b, h)
                 assert np.all(got[b, h][min(k, n):] == -1)
+
+
+@pytest.mark.parametrize("n,kind", [(40000, "normal"), (9000, "tied"), (70000, "tied"), (32768, "normal"),
+                                    (5000, "two-values")])
+def test_select_topk_paths(n, kind):
+    """Register-resident and re-read rows, candidate list and its all-keys fallback (heavy ties)."""
+    rng = np.random.default_rng(n)
+    B, H = 2, 3
+    if kind == "normal":
+        s = (rng.standard_normal((B, H, n)) * 2).astype(np.float32)
+    elif kind == "tied":
+        s = np.full((B, H, n), 0.75, dtype=np.float32)
+        s[..., rng.integers(0, n, size=n // 50)] = 3.0
+        s[..., rng.integers(0, n, size=n // 50)] = -1.0
+    else:
+        s = rng.choice(np.array([1.0, 2.0], dtype=np.float32), size=(B, H, n))
+    lens = np.array([n, n - 333], dtype=np.int32)
+    for k in (1, 257, 4096, n - 400):
+        idx = ppsa.select_topk(torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV), k)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                m = int(lens[b])
+                want = oracle.select_topk(s[b, h, :m], k)
+                g = got[b, h]
+                assert np.array_equal(np.sort(g[g >= 0]), np.sort(want[want >= 0])), (n, kind, k, b, h)
+                assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, m):] == -1)
 
 
 def test_full_size_bench_workload_sampled():
