@@ -55,9 +55,9 @@ constexpr int kMaxSparseRowsMfma = 2048;
 constexpr float kLazyLog2 = 8.0f;
 
 struct Tile {
-  uint4 k[2][4];   // [block][t]: K[row 16*blk + n][32t + 8g .. +8]
-  uint4 v[2][4];   // [block][i]: V[row 16*blk + 4g + i][8n .. +8]
-  bool valid[2][4];  // row 16*blk + 4g + i is live
+  uint4 k[2][4];    // [block][c]: K[row 16*blk + n][32c + 8g .. +8]
+  uint4 v[2][4];    // [block][i]: V[row 16*blk + 4g + i][8n .. +8]
+  uint32_t valid;   // bit 4*blk + i: row 16*blk + 4g + i is live
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -66,9 +66,16 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return (uint32_t)bf16_round(lo) | ((uint32_t)bf16_round(hi) << 16);
 }
 
+// 16 bytes at a byte offset from a base every lane shares: 32-bit offsets let the loads
+// use a scalar base plus one vector register per address.
+__device__ __forceinline__ uint4 load16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
 template <int MODE>
-__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uint16_t* vb, int tslot, int slot0,
+__device__ __forceinline__ void load_tile(Tile& t, const char* kb, const char* vb, int tslot, int slot0,
                                           int slot_end, const int32_t* rows, int g, int n) {
+  t.valid = 0u;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     {
@@ -80,9 +87,9 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
       } else {
         row = slot < slot_end ? slot : slot_end - 1;
       }
-      const uint16_t* kp = kb + (size_t)row * kD + 8 * g;
+      const uint32_t off = (uint32_t)row * (kD * 2) + 16u * g;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) t.k[blk][c] = *reinterpret_cast<const uint4*>(kp + 32 * c);
+      for (int c = 0; c < 4; ++c) t.k[blk][c] = load16(kb, off + 64u * c);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -97,8 +104,8 @@ __device__ __forceinline__ void load_tile(Tile& t, const uint16_t* kb, const uin
         ok = slot < slot_end;
         row = ok ? slot : slot_end - 1;
       }
-      t.valid[blk][i] = ok;
-      t.v[blk][i] = *reinterpret_cast<const uint4*>(vb + (size_t)row * kD + 8 * n);
+      t.valid |= (uint32_t)ok << (4 * blk + i);
+      t.v[blk][i] = load16(vb, (uint32_t)row * (kD * 2) + 16u * n);
     }
   }
 }
@@ -108,7 +115,7 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
   extern __shared__ float dyn[];  // [kWaves][group][kD] wave outputs, then staged sparse positions
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
@@ -122,8 +129,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
 
   const int n_live = min(max(a.seq_lens[b], 0), a.max_len);
   const size_t unit = (size_t)b * a.kv_heads + kv;
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k) + unit * (size_t)a.max_len * kD;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v) + unit * (size_t)a.max_len * kD;
+  // Unit bases; rows are addressed by 32-bit byte offsets (Nmax * 256 bytes < 4 GiB).
+  const char* kb = reinterpret_cast<const char*>(a.k) + unit * (size_t)a.max_len * kD * 2;
+  const char* vb = reinterpret_cast<const char*>(a.v) + unit * (size_t)a.max_len * kD * 2;
   const int slot0 = split * a.rows_per_split;
   int slot_end = MODE == MODE_SPARSE ? min(slot0 + a.rows_per_split, a.kslots)
                                      : min(slot0 + a.rows_per_split, n_live);
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float tot = group_sum<16>(s[blk][j]);  // heads past the group contribute exact zeros
-          if (n == 0 && cur.valid[blk][j]) a.scores[unit * (size_t)a.max_len + tslot + 16 * blk + 4 * g + j] = tot * a.scale;
+          if (n == 0 && ((cur.valid >> (4 * blk + j)) & 1u)) a.scores[unit * (size_t)a.max_len + tslot + 16 * blk + 4 * g + j] = tot * a.scale;
         }
     }
     float x[2][4];
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[blk][j] = cur.valid[blk][j] ? s[blk][j] * a.scale_log2 : -INFINITY;
+        x[blk][j] = ((cur.valid >> (4 * blk + j)) & 1u) ? s[blk][j] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, x[blk][j]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -222,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // One tile in flight per wave; occupancy (several waves per SIMD) hides the latency.
+  // One tile in flight per wave; occupancy (several waves per SIMD) hides the latency. Two
+  // tiles per wave at two waves per SIMD, and a software-pipelined loop, measured slower.
   for (int ti = wave; ti < ntiles; ti += kWaves) {
     Tile t;
     load_tile<MODE>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);

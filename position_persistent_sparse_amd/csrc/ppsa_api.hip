@@ -17,8 +17,11 @@ namespace ppsa {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kFullTargetGroups = 2048;   // workgroups a full layer is split into, about
-constexpr int kSparseTargetGroups = 1024; // same for a sparse layer
+// Workgroups a layer is cut into, about (MI355X: 256 CUs). Measured on the LLaMA-3-8B GQA
+// 32K shape: one long run per CU is fastest for full layers (fewest partials, fewest
+// concurrent DRAM streams); gathered sparse layers want two workgroups per CU.
+constexpr int kFullTargetGroups = 256;
+constexpr int kSparseTargetGroups = 512;
 constexpr int kMaxGridYZ = 65535;
 
 
@@ -30,7 +33,9 @@ bool use_mfma(const ppsa_dims& d) {
     const char* e = getenv("PPSA_ATTN_IMPL");
     return e && strcmp(e, "valu") == 0;
   }();
-  return !force_valu && attn_mfma_supported(d.dtype, d.head_dim, d.num_q_heads / d.num_kv_heads);
+  // The matrix-core pass addresses rows by 32-bit byte offsets within a (batch row, KV head).
+  const bool offsets_fit = (int64_t)d.max_seq_len * d.head_dim * 2 < (int64_t(1) << 32);
+  return !force_valu && offsets_fit && attn_mfma_supported(d.dtype, d.head_dim, d.num_q_heads / d.num_kv_heads);
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
