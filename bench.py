@@ -4,17 +4,20 @@ Times whole decode steps (every layer of the schedule: full, full + top-k
 selection, sparse) through the C ABI entry point ppsa_decode_step, with all
 inputs resident in HBM, and prints one JSON line: achieved KV GB/s (the
 algorithmic K+V bytes a step must read, divided by the step time), step
-microseconds, the fraction of the 8 TB/s HBM peak, a per-layer-kind
-breakdown, the roofline of the dominant kernel and the float64 CPU oracle
-timed over the same decode step on one host thread.
+microseconds, the fraction of the 8 TB/s HBM peak, per-kernel durations from
+the library's launch timing (HIP events around each launch, on the stream the
+kernels run on), the roofline of the dominant kernel, and the float64 CPU
+oracle timed over the same decode step on one host thread.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +26,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "PPSA decode-step attention µs and achieved KV GB/s (% of HBM peak)"
+EVICT_BYTES = 1 << 30  # written between per-step timings: larger than the last-level cache
+# Sources of the matrix-core attention kernel: the HBM traffic counted for it holds only while they are unchanged.
+ATTN_SOURCES = ("attn_mfma.hip", "attn_epilogue.h", "device_common.h", "ppsa_internal.h")
 
 
 def log(msg):
@@ -36,8 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--breakdown-steps", type=int, default=None)
-    p.add_argument("--copy-probe", action="store_true", help="also time a plain device copy of known size")
+    p.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB device copy (PMC calibration)")
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (counter-collection runs)")
     return p.parse_args()
 
 
@@ -72,6 +78,37 @@ class OracleTimer:
                           f"timed calls"}
 
 
+def attn_source_digest():
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "position_persistent_sparse_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel_key):
+    """HBM bytes per launch of `kernel_key` from the committed counter summary, or (None, reason)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None, f"no counter summary for {workload}"
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None, f"{os.path.basename(path)} has no json block"
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_key") != kernel_key:
+        return None, f"counters were taken for {rec.get('kernel_key')}, not {kernel_key}"
+    if rec.get("source_sha256") != attn_source_digest():
+        return None, "attention kernel sources changed since the counters were taken"
+    b = (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] + rec["write_kib_per_dispatch"] * rec["write_scale"]) * 1024
+    return int(round(b)), os.path.basename(path)
+
+
+def percentile(xs, p):
+    import numpy as np
+
+    return float(np.percentile(np.asarray(xs), p))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -104,66 +141,113 @@ def main():
     out = torch.empty_like(q)
     idx = torch.empty((n_sel, wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32, device=dev)
     codes = ppsa.schedule_codes(sched)
+    stream = torch.cuda.current_stream(dev)
+    step_bytes = synth.step_kv_bytes(wl, gen.seq_lens)
 
     def step():
         ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+
+    # 1. The timed region: K back-to-back steps.
+    start, end = ev(), ev()
+    start.record(stream)
     for _ in range(args.steps):
         step()
-    end.record()
+    end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    step_bytes = synth.step_kv_bytes(wl, gen.seq_lens)
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
 
-    # Per-layer-kind breakdown: the same kernels, one entry-point call per layer, HIP events around each call on
-    # the stream the kernels run on (torch's current stream).
-    bsteps = args.breakdown_steps or max(3, min(args.steps, 10))
-    per_kind = {"F": [], "X": [], "S": []}
-    stream = torch.cuda.current_stream(dev)
-    for it in range(bsteps + 1):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers + 1)]
-        evs[0].record(stream)
-        sel = -1
-        for layer, kind in enumerate(sched):
-            if kind == "F":
-                ppsa.full_attn(q[layer], k[layer], v[layer], lens, out=out[layer], workspace=ws)
-            elif kind == "X":
-                sel += 1
-                ppsa.full_attn_select(q[layer], k[layer], v[layer], lens, wl.topk, out=out[layer], idx=idx[sel],
-                                      workspace=ws)
-            else:
-                ppsa.sparse_attn(q[layer], k[layer], v[layer], lens, idx[sel], out=out[layer], workspace=ws)
-            evs[layer + 1].record(stream)
+    # 2. Per-step times, each step preceded (outside its events) by a 1 GiB write that evicts the caches.
+    scratch = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    per_step = []
+    for i in range(args.steps):
+        scratch.fill_(i & 0xFF)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        step()
+        e1.record(stream)
         torch.cuda.synchronize()
-        if it == 0:
-            continue  # warm-up pass
-        for layer, kind in enumerate(sched):
-            per_kind[kind].append(evs[layer].elapsed_time(evs[layer + 1]) * 1e3)
-    avg = {kk: float(np.mean(vv)) for kk, vv in per_kind.items() if vv}
-    layer_bytes = {kk: synth.layer_kv_bytes(wl, kk, gen.seq_lens) for kk in avg}
-    totals = {kk: avg[kk] * sched.count(kk) for kk in avg}
-    breakdown = {kk: {"layers": sched.count(kk), "us_per_layer": round(avg[kk], 2),
-                      "GB_per_s": round(layer_bytes[kk] / (avg[kk] * 1e-6) / 1e9, 1),
-                      "hbm_frac": round(layer_bytes[kk] / (avg[kk] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-                 for kk in avg}
-    sel_overhead_us = n_sel * (avg.get("X", 0.0) - avg.get("F", avg.get("X", 0.0)))
-    dominant = max(("F", "S"), key=lambda kk: totals.get(kk, 0.0))
-    if dominant == "F" and "F" not in avg:
-        dominant = "X"
-    kname = {"F": "full attention layer (split-N attention + combine)",
-             "X": "full attention + selection layer",
-             "S": "sparse attention layer (gathered split attention + combine)"}[dominant]
-    achieved = layer_bytes[dominant] / (avg[dominant] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "bytes_per_launch": layer_bytes[dominant], "us_per_launch": round(avg[dominant], 2)}
+        per_step.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    log(f"evicted steps: median {percentile(per_step, 50):.1f} us")
+
+    # 3. Per-kernel durations: the library's launch timing (two HIP events around each launch).
+    launches_per_step = 2 * len(sched) + n_sel
+    ppsa.timing_enable(launches_per_step * args.steps)
+    try:
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        timed = ppsa.timing_read()
+    finally:
+        ppsa.timing_enable(0)
+    instrumented_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    kernels = {}
+    for key in ppsa.KERNEL_KEYS:
+        n, ms = timed[key]
+        if n:
+            kernels[key] = {"launches_per_step": round(n / args.steps, 2), "us_per_launch": round(ms * 1e3 / n, 2),
+                            "us_per_step": round(ms * 1e3 / args.steps, 1)}
+    layer_bytes = {"attn_full": synth.layer_kv_bytes(wl, "F", gen.seq_lens),
+                   "attn_full_scores": synth.layer_kv_bytes(wl, "X", gen.seq_lens),
+                   "attn_sparse": synth.layer_kv_bytes(wl, "S", gen.seq_lens)}
+    for key, b in layer_bytes.items():
+        if key in kernels:
+            gb = b / (kernels[key]["us_per_launch"] * 1e-6) / 1e9
+            kernels[key].update({"kv_bytes_per_launch": b, "GB_per_s": round(gb, 1),
+                                 "hbm_frac": round(gb / HBM_PEAK_GBS, 4)})
+
+    # 4. The same step replayed from a captured HIP graph.
+    graph_us = None
+    try:
+        if args.no_graph:
+            raise RuntimeError("skipped (--no-graph)")
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = round(e0.elapsed_time(e1) * 1e3 / args.steps, 1)
+        del graph
+    except Exception as exc:  # reported, never fatal: the eager step is the measurement
+        log(f"graph replay not measured: {exc}")
+
+    # Roofline of the attention kernel with the largest share of the step.
+    attn_keys = [kk for kk in layer_bytes if kk in kernels]
+    dom = max(attn_keys, key=lambda kk: kernels[kk]["us_per_step"])
+    traffic, traffic_src = measured_traffic(wl.name, dom)
+    roofline = {"bound": "hbm", "kernel": f"{dom}: {ppsa.timing_kernel_name(ppsa.KERNEL_KEYS.index(dom))}",
+                "achieved": kernels[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kernels[dom]["hbm_frac"], "traffic": traffic, "traffic_source": traffic_src,
+                "bytes_per_launch": layer_bytes[dom], "us_per_launch": kernels[dom]["us_per_launch"],
+                "launches_per_step": kernels[dom]["launches_per_step"]}
+
+    sel_us = kernels.get("select", {}).get("us_per_step", 0.0)
+    if "attn_full_scores" in kernels and "attn_full" in kernels:
+        sel_us += n_sel * (kernels["attn_full_scores"]["us_per_launch"] - kernels["attn_full"]["us_per_launch"])
 
     copy_probe = None
     if args.copy_probe:
@@ -171,11 +255,11 @@ def main():
         src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
         for _ in range(10):
             dst.copy_(src)
-        e1.record()
+        e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / 10
         copy_probe = {"bytes_read": n, "bytes_written": n, "us": round(us, 1),
@@ -203,8 +287,12 @@ def main():
         "step_us": round(ms_per_step * 1e3, 1),
         "kv_bytes_per_step": step_bytes,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "selection_overhead_frac": round(sel_overhead_us / (ms_per_step * 1e3), 4),
-        "breakdown": breakdown,
+        "step_us_evicted": {"median": round(percentile(per_step, 50), 1), "p10": round(percentile(per_step, 10), 1),
+                            "p90": round(percentile(per_step, 90), 1)},
+        "step_us_graph_replay": graph_us,
+        "step_us_with_launch_timing": round(instrumented_us, 1),
+        "selection_overhead_frac": round(sel_us / (ms_per_step * 1e3), 4),
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -55,7 +55,7 @@ typedef enum ppsa_status {
   PPSA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim, group size, dtype */
   PPSA_ERR_WORKSPACE = -3,   /* workspace smaller than ppsa_workspace_bytes() */
   PPSA_ERR_SCHEDULE = -4,    /* decode schedule: unknown kind, or sparse before any selection */
-  PPSA_ERR_HIP = -5          /* a kernel launch failed */
+  PPSA_ERR_HIP = -5          /* a HIP runtime call failed (kernel launch, event) */
 } ppsa_status;
 
 typedef enum ppsa_dtype { PPSA_F32 = 0, PPSA_BF16 = 1 } ppsa_dtype;
@@ -144,6 +144,42 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
 int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Launch timing (instrumentation; not part of the method). While timing is
+ * on, every kernel the entry points above enqueue is bracketed by two HIP
+ * events recorded on the same stream, and ppsa_timing_read() returns, per
+ * kernel kind, how many launches completed and their summed elapsed time
+ * (begin event to end event) since the previous read.
+ *
+ * ppsa_timing_enable(capacity): capacity > 0 switches timing on with a pool
+ * of events for `capacity` launches between reads (created here, the only
+ * allocation); a launch that finds the pool empty is not timed and counts as
+ * dropped. capacity == 0 switches timing off and destroys the pool. Either
+ * call first waits for launches still pending. Returns PPSA_OK,
+ * PPSA_ERR_INVALID_ARG (capacity < 0) or PPSA_ERR_HIP.
+ *
+ * ppsa_timing_read(counts, total_ms, num_kinds, dropped): host arrays of
+ * num_kinds >= PPSA_KERNEL_KINDS entries, indexed by ppsa_kernel_kind;
+ * dropped (host, may be NULL) receives the number of untimed launches. Waits
+ * for the recorded events (this call synchronises). Returns PPSA_OK,
+ * PPSA_ERR_INVALID_ARG or PPSA_ERR_HIP.
+ *
+ * Timing state is process-wide. Do not read while another thread enqueues.
+ */
+typedef enum ppsa_kernel_kind {
+  PPSA_KERNEL_ATTN_FULL = 0,        /* split attention pass of a full layer */
+  PPSA_KERNEL_ATTN_FULL_SCORES = 1, /* the same pass writing selection scores */
+  PPSA_KERNEL_ATTN_SPARSE = 2,      /* split attention pass over selected rows */
+  PPSA_KERNEL_COMBINE = 3,          /* merge of split partials */
+  PPSA_KERNEL_SELECT = 4,           /* top-k selection */
+  PPSA_KERNEL_KINDS = 5
+} ppsa_kernel_kind;
+
+int ppsa_timing_enable(int32_t capacity);
+int ppsa_timing_read(int32_t* counts, double* total_ms, int32_t num_kinds, int64_t* dropped);
+/* Static description of a kernel kind ("unknown" outside the enum). */
+const char* ppsa_timing_kernel_name(int32_t kind);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,8 @@ PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
+PPSA_KERNEL_KINDS = 5
+KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select")  # ppsa_kernel_kind order
 
 
 class Dims(ctypes.Structure):
@@ -55,8 +57,12 @@ def _load():
     lib.ppsa_select_topk.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.ppsa_timing_enable.argtypes = [i32]
+    lib.ppsa_timing_read.argtypes = [vp, vp, i32, vp]
+    lib.ppsa_timing_kernel_name.argtypes = [i32]
+    lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
-                 "ppsa_decode_step"):
+                 "ppsa_decode_step", "ppsa_timing_enable", "ppsa_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -199,6 +205,26 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
                                  _ptr(seq_lens), int(topk), _ptr(out), _ptr(idx), _ptr(scores), _ptr(ws),
                                  ws.numel(), _stream(q.device)), "ppsa_decode_step")
     return out, idx
+
+
+def timing_enable(capacity: int):
+    """Switch launch timing on with an event pool for `capacity` launches (0 switches it off)."""
+    _check(_lib.ppsa_timing_enable(int(capacity)), "ppsa_timing_enable")
+
+
+def timing_read() -> dict:
+    """{kernel key: (launches, total ms)} since the previous read, plus "dropped" (untimed launches)."""
+    counts = (ctypes.c_int32 * PPSA_KERNEL_KINDS)()
+    ms = (ctypes.c_double * PPSA_KERNEL_KINDS)()
+    dropped = ctypes.c_int64()
+    _check(_lib.ppsa_timing_read(counts, ms, PPSA_KERNEL_KINDS, ctypes.byref(dropped)), "ppsa_timing_read")
+    res = {key: (int(counts[i]), float(ms[i])) for i, key in enumerate(KERNEL_KEYS)}
+    res["dropped"] = int(dropped.value)
+    return res
+
+
+def timing_kernel_name(kind: int) -> str:
+    return _lib.ppsa_timing_kernel_name(int(kind)).decode()
 
 
 def raw_library():

@@ -133,6 +133,16 @@ AttnArgs base_args(const Ctx& c, const void* q, const void* k, const void* v, co
 
 int finish(hipError_t e) { return e == hipSuccess ? PPSA_OK : PPSA_ERR_HIP; }
 
+// Runs launch() between the two events of a timed launch when timing is on.
+template <typename F>
+hipError_t timed(int kind, hipStream_t stream, F&& launch) {
+  hipEvent_t end = nullptr;
+  const int token = timing_begin(stream, &end);
+  const hipError_t e = launch();
+  timing_end(token, e == hipSuccess ? kind : -1, end, stream);
+  return e;
+}
+
 // Merge pass after a multi-split attention launch (a single split writes out itself).
 int run_combine(const Ctx& c, int splits, void* out) {
   if (splits <= 1) return PPSA_OK;
@@ -143,7 +153,7 @@ int run_combine(const Ctx& c, int splits, void* out) {
   cb.out = out;
   cb.rows = c.d->batch * c.d->num_q_heads;
   cb.splits = splits;
-  return finish(launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream));
+  return finish(timed(KERNEL_COMBINE, c.stream, [&] { return launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream); }));
 }
 
 int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx) {
@@ -155,7 +165,7 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
   s.kv_heads = c.d->num_kv_heads;
   s.max_len = c.d->max_seq_len;
   s.topk = topk;
-  return finish(launch_select(s, c.stream));
+  return finish(timed(KERNEL_SELECT, c.stream, [&] { return launch_select(s, c.stream); }));
 }
 
 int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
@@ -166,8 +176,9 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
   const bool select = idx != nullptr;
   if (select) a.scores = scores ? scores : reinterpret_cast<float*>(c.ws + c.plan.off_scores);
   const int mode = select ? MODE_FULL_SCORES : MODE_FULL;
-  int rc = finish(c.plan.mfma ? launch_attn_mfma(a, mode, c.stream)
-                              : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream));
+  int rc = finish(timed(select ? KERNEL_ATTN_FULL_SCORES : KERNEL_ATTN_FULL, c.stream, [&] {
+    return c.plan.mfma ? launch_attn_mfma(a, mode, c.stream) : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream);
+  }));
   if (rc == PPSA_OK) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
   return run_select(c, a.scores, seq_lens, topk, idx);
@@ -180,8 +191,10 @@ int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const 
   a.kslots = topk;
   a.splits = c.plan.sparse_splits;
   a.rows_per_split = c.plan.sparse_rows;
-  const int rc = finish(c.plan.mfma ? launch_attn_mfma(a, MODE_SPARSE, c.stream)
-                                    : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream));
+  const int rc = finish(timed(KERNEL_ATTN_SPARSE, c.stream, [&] {
+    return c.plan.mfma ? launch_attn_mfma(a, MODE_SPARSE, c.stream)
+                       : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream);
+  }));
   return rc == PPSA_OK ? run_combine(c, a.splits, out) : rc;
 }
 
@@ -216,7 +229,7 @@ const char* ppsa_status_string(int status) {
     case PPSA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PPSA_ERR_WORKSPACE: return "workspace too small";
     case PPSA_ERR_SCHEDULE: return "invalid decode schedule";
-    case PPSA_ERR_HIP: return "HIP kernel launch failed";
+    case PPSA_ERR_HIP: return "HIP runtime call failed";
     default: return "unknown status";
   }
 }

@@ -74,4 +74,18 @@ hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hip
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
+// Launch timing (timing.hip). Kinds match the public PPSA_KERNEL_* values.
+enum KernelKind : int {
+  KERNEL_ATTN_FULL = 0,
+  KERNEL_ATTN_FULL_SCORES = 1,
+  KERNEL_ATTN_SPARSE = 2,
+  KERNEL_COMBINE = 3,
+  KERNEL_SELECT = 4,
+  KERNEL_KINDS = 5
+};
+// Records a begin event on `stream` when timing is on; returns a token (-1: untimed) and the end event.
+int timing_begin(hipStream_t stream, hipEvent_t* end);
+// Records the end event of a timed launch of `kind`.
+void timing_end(int token, int kind, hipEvent_t end, hipStream_t stream);
+
 }  // namespace ppsa

@@ -133,3 +133,22 @@ def test_empty_batch_and_empty_schedule_are_noops():
     assert full(d, q=None, k=None, v=None, lens=None, out=None, ws=None, ws_bytes=0) == ppsa.PPSA_OK
     assert LIB.ppsa_decode_step(ctypes.byref(dims()), 0, None, None, None, None, None, 0, None, None, None, None,
                                 0, None) == ppsa.PPSA_OK
+
+
+def test_timing_api_without_gpu_work():
+    # Switching off (no pool) and reading with nothing recorded make no HIP call.
+    assert LIB.ppsa_timing_enable(0) == ppsa.PPSA_OK
+    assert LIB.ppsa_timing_enable(-1) == ppsa.PPSA_ERR_INVALID_ARG
+    res = ppsa.timing_read()
+    assert res["dropped"] == 0
+    assert all(res[k] == (0, 0.0) for k in ppsa.KERNEL_KEYS)
+    counts = (ctypes.c_int32 * 5)()
+    ms = (ctypes.c_double * 5)()
+    assert LIB.ppsa_timing_read(counts, ms, 4, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(None, ms, 5, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(counts, None, 5, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(counts, ms, 5, None) == ppsa.PPSA_OK
+    names = [ppsa.timing_kernel_name(i) for i in range(ppsa.PPSA_KERNEL_KINDS)]
+    assert len(set(names)) == ppsa.PPSA_KERNEL_KINDS and "unknown" not in names
+    assert ppsa.timing_kernel_name(ppsa.PPSA_KERNEL_KINDS) == "unknown"
+    assert ppsa.timing_kernel_name(-1) == "unknown"
