@@ -46,8 +46,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kWaves = 4;                      // waves per workgroup, multi-split launches
+constexpr int kWavesSingle = 8;                // one split per unit: fewer, longer workgroups
 constexpr int kD = 128;
 constexpr int kTile = 32;
 constexpr int kRowsTrip = kTile * kWaves;
@@ -114,14 +114,15 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
   return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
-  extern __shared__ float dyn[];  // [kWaves][group][kD] wave outputs, then staged sparse positions
-  __shared__ float sm_m[kWaves][kMaxGroup];
-  __shared__ float sm_l[kWaves][kMaxGroup];
+template <int MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int kThreads = WAVES * kWave;
+  extern __shared__ float dyn[];  // [WAVES][group][kD] wave outputs, then staged sparse positions
+  __shared__ float sm_m[WAVES][kMaxGroup];
+  __shared__ float sm_l[WAVES][kMaxGroup];
   const int group = a.group;
   float* sm_o = dyn;
-  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + kWaves * group * kD);
+  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * group * kD);
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // One tile in flight per wave; occupancy (several waves per SIMD) hides the latency. Two
   // tiles per wave at two waves per SIMD, and a software-pipelined loop, measured slower.
-  for (int ti = wave; ti < ntiles; ti += kWaves) {
+  for (int ti = wave; ti < ntiles; ti += WAVES) {
     Tile t;
     load_tile<MODE>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
     process(t, ti);
@@ -261,11 +262,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int h = i / kD, d = i % kD;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][h]);
     const float ms = mx == -INFINITY ? 0.0f : mx;
     float o = 0.0f, lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       const float c = exp2_fast(sm_m[w][h] - ms);
       o += sm_o[(w * group + h) * kD + d] * c;
       lsum += sm_l[w][h] * c;
@@ -293,20 +294,37 @@ bool attn_mfma_supported(int dtype, int head_dim, int group) {
   return dtype == PPSA_BF16 && head_dim == kD && group >= 1 && group <= kMaxGroup;
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream) {
-  if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
-  if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRowsMfma) return hipErrorInvalidValue;
-  // Wave partial outputs, then the staged sparse positions.
-  size_t lds = (size_t)kWaves * a.group * kD * sizeof(float);
-  if (mode == MODE_SPARSE) lds += (size_t)a.rows_per_split * sizeof(int32_t);
-  dim3 grid(a.splits, a.kv_heads, a.batch), block(kThreads);
+namespace {
+
+template <int WAVES>
+hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t stream) {
+  const dim3 grid(a.splits, a.kv_heads, a.batch), block(WAVES * kWave);
   switch (mode) {
-    case MODE_FULL: attn_mfma_kernel<MODE_FULL><<<grid, block, lds, stream>>>(a); break;
-    case MODE_FULL_SCORES: attn_mfma_kernel<MODE_FULL_SCORES><<<grid, block, lds, stream>>>(a); break;
-    case MODE_SPARSE: attn_mfma_kernel<MODE_SPARSE><<<grid, block, lds, stream>>>(a); break;
+    case MODE_FULL: attn_mfma_kernel<MODE_FULL, WAVES><<<grid, block, lds, stream>>>(a); break;
+    case MODE_FULL_SCORES: attn_mfma_kernel<MODE_FULL_SCORES, WAVES><<<grid, block, lds, stream>>>(a); break;
+    case MODE_SPARSE: attn_mfma_kernel<MODE_SPARSE, WAVES><<<grid, block, lds, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions.
+size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
+  size_t lds = (size_t)waves * a.group * kD * sizeof(float);
+  if (mode == MODE_SPARSE) lds += (size_t)a.rows_per_split * sizeof(int32_t);
+  return lds;
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream) {
+  if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
+  if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRowsMfma) return hipErrorInvalidValue;
+  // One split per unit means one workgroup per unit: twice the waves keep more rows in flight per CU
+  // (measured 8-10 % faster there), while LDS stays within 64 KiB.
+  if (a.splits == 1 && lds_bytes(a, mode, kWavesSingle) <= 65536)
+    return launch_waves<kWavesSingle>(a, mode, lds_bytes(a, mode, kWavesSingle), stream);
+  return launch_waves<kWaves>(a, mode, lds_bytes(a, mode, kWaves), stream);
 }
 
 }  // namespace ppsa

@@ -181,9 +181,12 @@ def test_select_topk_on_crafted_scores():
 
 
 @pytest.mark.parametrize("n,kind", [(40000, "normal"), (9000, "tied"), (70000, "tied"), (32768, "normal"),
-                                    (5000, "two-values")])
+                                    (5000, "two-values"), (20000, "cluster"), (12000, "outlier"), (9000, "inf"),
+                                    (6000, "huge")])
 def test_select_topk_paths(n, kind):
-    """Register-resident and re-read rows, candidate list and its all-keys fallback (heavy ties)."""
+    """Register-resident and re-read rows; threshold bucket resolved by pairwise ranking (normal), by
+    radix digits over its candidates (two-values, cluster, huge: a range too wide for float32 puts
+    every score in one bucket) or over all keys (tied, outlier: bucket larger than the LDS list)."""
     rng = np.random.default_rng(n)
     B, H = 2, 3
     if kind == "normal":
@@ -192,6 +195,18 @@ def test_select_topk_paths(n, kind):
         s = np.full((B, H, n), 0.75, dtype=np.float32)
         s[..., rng.integers(0, n, size=n // 50)] = 3.0
         s[..., rng.integers(0, n, size=n // 50)] = -1.0
+    elif kind == "cluster":  # 5000 scores inside one bucket around the 4096-th largest
+        s = rng.uniform(0.0, 1.0, size=(B, H, n)).astype(np.float32)
+        s[..., rng.permutation(n)[:5000]] = (0.9 + 1e-5 * rng.uniform(size=5000)).astype(np.float32)
+    elif kind == "outlier":
+        s = (rng.standard_normal((B, H, n)) * 2).astype(np.float32)
+        s[..., 7], s[..., 11] = 1e30, -1e30
+    elif kind == "inf":
+        s = (rng.standard_normal((B, H, n)) * 2).astype(np.float32)
+        s[..., rng.integers(0, n, size=40)] = np.inf
+        s[..., rng.integers(0, n, size=40)] = -np.inf
+    elif kind == "huge":
+        s = rng.uniform(-3e38, 3e38, size=(B, H, n)).astype(np.float32)
     else:
         s = rng.choice(np.array([1.0, 2.0], dtype=np.float32), size=(B, H, n))
     lens = np.array([n, n - 333], dtype=np.int32)
