@@ -52,6 +52,10 @@ constexpr int kD = 128;
 constexpr int kTile = 32;
 constexpr int kRowsTrip = kTile * kWaves;
 constexpr int kMaxSparseRowsMfma = 2048;
+// Scores of a full+scores split are gathered in LDS and written once the split is done (one
+// coalesced pass instead of a few bytes per tile amid the K/V stream, which cost 10-15 % of the
+// layer); a split's LDS (wave outputs + scores) stays within 64 KiB.
+constexpr size_t kMaxLdsBytes = 65536;
 constexpr float kLazyLog2 = 8.0f;
 
 struct Tile {
@@ -122,7 +126,8 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   __shared__ float sm_l[WAVES][kMaxGroup];
   const int group = a.group;
   float* sm_o = dyn;
-  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * group * kD);
+  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * group * kD);  // sparse mode
+  float* sm_sc = dyn + WAVES * group * kD;                                    // full+scores mode
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float tot = group_sum<16>(s[blk][j]);  // heads past the group contribute exact zeros
-          if (n == 0 && ((cur.valid >> (4 * blk + j)) & 1u)) a.scores[unit * (size_t)a.max_len + tslot + 16 * blk + 4 * g + j] = tot * a.scale;
+          if (n == 0) sm_sc[tslot - slot0 + 16 * blk + 4 * g + j] = tot * a.scale;
         }
     }
     float x[2][4];
@@ -256,6 +261,10 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
     }
   }
   __syncthreads();
+  if constexpr (MODE == MODE_FULL_SCORES) {
+    float* dst = a.scores + unit * (size_t)a.max_len + slot0;
+    for (int i = tid; i < slot_end - slot0; i += kThreads) dst[i] = sm_sc[i];
+  }
 
   const bool single = a.splits == 1;
   for (int i = tid; i < group * kD; i += kThreads) {
@@ -289,6 +298,9 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 
 int attn_mfma_rows_granule() { return kRowsTrip; }
 int attn_mfma_max_sparse_rows() { return kMaxSparseRowsMfma; }
+int attn_mfma_max_score_rows(int group) {
+  return (int)((kMaxLdsBytes - (size_t)kWaves * group * kD * sizeof(float)) / sizeof(float)) / kRowsTrip * kRowsTrip;
+}
 
 bool attn_mfma_supported(int dtype, int head_dim, int group) {
   return dtype == PPSA_BF16 && head_dim == kD && group >= 1 && group <= kMaxGroup;
@@ -308,10 +320,10 @@ hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t str
   return hipGetLastError();
 }
 
-// Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions.
+// Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions or scores.
 size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
   size_t lds = (size_t)waves * a.group * kD * sizeof(float);
-  if (mode == MODE_SPARSE) lds += (size_t)a.rows_per_split * sizeof(int32_t);
+  if (mode == MODE_SPARSE || mode == MODE_FULL_SCORES) lds += (size_t)a.rows_per_split * 4;
   return lds;
 }
 
@@ -320,9 +332,10 @@ size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
 hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream) {
   if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
   if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRowsMfma) return hipErrorInvalidValue;
+  if (mode == MODE_FULL_SCORES && lds_bytes(a, mode, kWaves) > kMaxLdsBytes) return hipErrorInvalidValue;
   // One split per unit means one workgroup per unit: twice the waves keep more rows in flight per CU
   // (measured 8-10 % faster there), while LDS stays within 64 KiB.
-  if (a.splits == 1 && lds_bytes(a, mode, kWavesSingle) <= 65536)
+  if (a.splits == 1 && lds_bytes(a, mode, kWavesSingle) <= kMaxLdsBytes)
     return launch_waves<kWavesSingle>(a, mode, lds_bytes(a, mode, kWavesSingle), stream);
   return launch_waves<kWaves>(a, mode, lds_bytes(a, mode, kWaves), stream);
 }

@@ -51,7 +51,8 @@ struct Plan {
   int sparse_rows = 0, sparse_splits = 0;
   int max_splits = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
-  bool ok = true;  // false: the budget needs more splits than one unit may have
+  bool full_ok = true;    // false: full layers would need more splits than one unit may have
+  bool sparse_ok = true;  // false: the budget needs more splits than one unit may have
   bool mfma = false;
 };
 
@@ -81,7 +82,9 @@ Plan make_plan(const ppsa_dims& d, int topk) {
   rows = std::max<int64_t>(rows, ceil_div(d.max_seq_len, kMaxSplitsPerUnit));
   if ((int64_t)d.max_seq_len * kv_row_bytes <= kSingleSplitBytes) rows = d.max_seq_len;
   p.full_rows = std::max(round_up(rows, granule), granule);
+  if (p.mfma) p.full_rows = std::min(p.full_rows, attn_mfma_max_score_rows(d.num_q_heads / d.num_kv_heads));
   p.full_splits = (int)ceil_div(d.max_seq_len, p.full_rows);
+  if (p.full_splits > kMaxSplitsPerUnit) p.full_ok = false;  // only with the score-staging cap, N > 2M rows
   if (topk > 0) {
     rows = ceil_div(units * topk, kSparseTargetGroups);
     rows = std::max<int64_t>(rows, ceil_div(topk, kMaxSplitsPerUnit));
@@ -89,7 +92,7 @@ Plan make_plan(const ppsa_dims& d, int topk) {
     const int cap = (p.mfma ? attn_mfma_max_sparse_rows() : attn_max_sparse_rows()) / granule * granule;
     p.sparse_rows = std::max(round_up(rows, granule), granule);
     if (p.sparse_rows > cap) {
-      p.ok = false;
+      p.sparse_ok = false;
       p.sparse_rows = cap;
     }
     p.sparse_splits = (int)ceil_div(topk, p.sparse_rows);
@@ -253,6 +256,7 @@ int ppsa_full_attn(const ppsa_dims* dims, const void* q, const void* k_cache, co
   if (dims->batch == 0) return PPSA_OK;
   if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
   Ctx c{dims, make_plan(*dims, 0), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (!c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
   return run_full(c, q, k_cache, v_cache, seq_lens, out, 0, nullptr, nullptr);
@@ -268,6 +272,7 @@ int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_ca
   if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
   if (!idx || !aligned(idx, 4) || (scores && !aligned(scores, 4))) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (!c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
   return run_full(c, q, k_cache, v_cache, seq_lens, out, topk, scores, idx);
@@ -297,7 +302,7 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
   if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
   if (!idx || !aligned(idx, 4)) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
-  if (!c.plan.ok) return PPSA_ERR_UNSUPPORTED;
+  if (!c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
   return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out);
@@ -309,12 +314,13 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if (num_layers < 0 || (num_layers > 0 && !schedule)) return PPSA_ERR_INVALID_ARG;
-  int n_sel = 0;
+  int n_sel = 0, n_sparse = 0;
   for (int l = 0; l < num_layers; ++l) {
     const int kind = schedule[l];
     if (kind == PPSA_FULL_SELECT) ++n_sel;
     else if (kind == PPSA_SPARSE) {
       if (n_sel == 0) return PPSA_ERR_SCHEDULE;
+      ++n_sparse;
     } else if (kind != PPSA_FULL) {
       return PPSA_ERR_SCHEDULE;
     }
@@ -326,7 +332,8 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
   if (scores && !aligned(scores, 4)) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0), static_cast<char*>(workspace),
         static_cast<hipStream_t>(stream)};
-  if (!c.plan.ok) return PPSA_ERR_UNSUPPORTED;
+  if (num_layers > n_sparse && !c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
+  if (n_sparse > 0 && !c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
 
   const size_t eb = elem_bytes(dims->dtype);

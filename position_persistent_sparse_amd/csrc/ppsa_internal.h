@@ -64,6 +64,7 @@ int attn_max_sparse_rows();
 bool attn_mfma_supported(int dtype, int head_dim, int group);
 int attn_mfma_rows_granule();
 int attn_mfma_max_sparse_rows();
+int attn_mfma_max_score_rows(int group);  // rows of one full-layer split (its scores are staged in LDS)
 hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream);
 // Largest group size the attention kernels take.
 constexpr int kMaxGroup = 16;

@@ -254,3 +254,31 @@ def test_full_size_bench_workload_sampled():
                 sc_h[sel, b:b + 1, h:h + 1] if kind == "X" else None,
                 idx_h[sel, b:b + 1, h:h + 1] if sel >= 0 else None, f"full-size layer {layer} unit {(b, h)}"))
     say(f"[parity] full-size {wl.name}: ok, max abs error {worst:.3e}")
+
+
+def test_selection_layer_at_score_staging_cap_sampled():
+    """Group 16 with 32 units at N = 70000: the planner's 8832-row splits exceed the 8192 rows whose
+    scores one workgroup can stage in LDS, so splits are capped at 8192 rows (9 per unit, ragged last
+    one). Scores, selection and outputs of sampled units are checked."""
+    wl = synth.Workload("score-cap", layers=3, batch=4, q_heads=128, kv_heads=8, head_dim=128, max_len=70000,
+                        topk=512, dtype="bf16", select_layers=(2,), seed=91, min_len=60000)
+    gen = synth.Generator(wl)
+    units = [(0, 0), (3, 7)]
+    say(f"[parity] score-cap: B={wl.batch} Hq={wl.q_heads} Hkv={wl.kv_heads} N={wl.max_len} "
+        f"lens={gen.seq_lens.tolist()}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV, keep_layers={2}, keep_units=units)
+    scores = torch.full((1, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32, device=DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores)
+    torch.cuda.synchronize()
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    g = wl.group
+    for (b, h) in units:
+        qg, kh, vh = host[2][(b, h)]
+        sub = wl.with_(batch=1, q_heads=g, kv_heads=1)
+        check_layer("X", sub, qg[None], kh[None, None], vh[None, None], gen.seq_lens[b:b + 1],
+                    out_h[2, b, h * g:(h + 1) * g][None], idx_h[0, b:b + 1, h:h + 1], sc_h[0, b:b + 1, h:h + 1],
+                    idx_h[0, b:b + 1, h:h + 1], f"score-cap unit {(b, h)}")
+    n_min = int(gen.seq_lens.min())
+    assert np.all(np.isfinite(sc_h[0, :, :, :n_min])), "a live score was not written"
+    say("[parity] score-cap: ok")
