@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB device copy (PMC calibration)")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (counter-collection runs)")
+    p.add_argument("--no-comparison", action="store_true", help="skip the dense and select-every-layer schedules")
     return p.parse_args()
 
 
@@ -235,6 +236,35 @@ def main():
     except Exception as exc:  # reported, never fatal: the eager step is the measurement
         log(f"graph replay not measured: {exc}")
 
+    # 5. Comparison schedules over the same inputs: every layer full (the dense decode step TidalDecode
+    # is measured against) and a selection at every layer after the first two.
+    comparison = {}
+    for name, sch in (("dense", ["F"] * wl.layers), ("select_every_layer", ["F", "F"] + ["X"] * (wl.layers - 2))):
+        if args.no_comparison or wl.layers < 3:
+            break
+        c_codes = ppsa.schedule_codes(sch)
+        n_x = sch.count("X")
+        c_idx = torch.empty((max(n_x, 1), wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32, device=dev)
+
+        def c_step():
+            ppsa.decode_step(sch, q, k, v, lens, wl.topk, out=out, idx=c_idx if n_x else None, workspace=ws,
+                             sched_codes=c_codes)
+
+        c_step()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            c_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        comparison[name] = {"schedule": "".join(sch), "step_us": round(us, 1),
+                            "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
+        del c_idx
+    if comparison:
+        log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
+
     # Roofline of the attention kernel with the largest share of the step.
     attn_keys = [kk for kk in layer_bytes if kk in kernels]
     dom = max(attn_keys, key=lambda kk: kernels[kk]["us_per_step"])
@@ -292,6 +322,7 @@ def main():
         "step_us_graph_replay": graph_us,
         "step_us_with_launch_timing": round(instrumented_us, 1),
         "selection_overhead_frac": round(sel_us / (ms_per_step * 1e3), 4),
+        "comparison_schedules": comparison or None,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -55,11 +55,15 @@ def check_step(wl, gen, name):
         f"N={wl.max_len} k={wl.topk} {wl.dtype} lens={gen.seq_lens.tolist()}")
     q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
     n_sel = wl.schedule().count("X")
-    scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32, device=DEV)
+    scores = None
+    if n_sel:
+        scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32,
+                            device=DEV)
     out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores)
     torch.cuda.synchronize()
     out_h = widen_out(torch_io.from_torch(out), wl)
-    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    idx_h = idx.cpu().numpy() if n_sel else None
+    sc_h = scores.cpu().numpy() if n_sel else None
     sel = -1
     worst = 0.0
     for layer, kind in enumerate(wl.schedule()):
@@ -77,6 +81,15 @@ def check_step(wl, gen, name):
 def test_decode_step_reduced(name):
     wl = REDUCED[name]
     check_step(wl, synth.Generator(wl), name)
+
+
+@pytest.mark.parametrize("kind", ["dense", "select-every-layer"])
+def test_comparison_schedules(kind):
+    """The two comparison schedules the benchmark times: every layer full (the dense baseline) and a
+    selection at every layer after the first two (a per-layer selection cost)."""
+    base = REDUCED["llama3-8b-gqa-32k"]
+    wl = base.with_(select_layers=() if kind == "dense" else tuple(range(2, base.layers)))
+    check_step(wl, synth.Generator(wl), f"{kind} {''.join(wl.schedule())}")
 
 
 def test_padding_poison_and_determinism():
