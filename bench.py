@@ -6,8 +6,10 @@ inputs resident in HBM, and prints one JSON line: achieved KV GB/s (the
 algorithmic K+V bytes a step must read, divided by the step time), step
 microseconds, the fraction of the 8 TB/s HBM peak, per-kernel durations from
 the library's launch timing (HIP events around each launch, on the stream the
-kernels run on), the roofline of the dominant kernel, and the float64 CPU
-oracle timed over the same decode step on one host thread.
+kernels run on), the roofline of the dominant kernel, the float64 CPU oracle
+timed over the same decode step on one host thread, and two comparison
+schedules over the same inputs (every layer full; a selection at every layer
+after the first two) with PPSA's speedup over each.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
