@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB device copy (PMC calibration)")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (counter-collection runs)")
     p.add_argument("--no-comparison", action="store_true", help="skip the dense and select-every-layer schedules")
+    p.add_argument("--no-multi-token", action="store_true", help="skip the multi-token (append + step) timing")
     return p.parse_args()
 
 
@@ -267,6 +268,30 @@ def main():
     if comparison:
         log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
 
+    # 6. Multi-token decode (last: it writes cache rows): T tokens, each appending its K/V rows and then
+    # running the step, each batch row starting T rows short of its length so that every token has room.
+    multi = None
+    if not args.no_multi_token:
+        T = args.steps
+        lens_mt = torch.clamp(lens - T, min=0).to(torch.int32)
+        kn = torch.randn((wl.layers, wl.batch, wl.kv_heads, wl.head_dim), device=dev).to(k.dtype)
+        vn = torch.randn_like(kn)
+
+        def token():
+            ppsa.append_kv(kn, vn, k, v, lens_mt)
+            ppsa.decode_step(sched, q, k, v, lens_mt, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes)
+
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(T):
+            token()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ok = bool(torch.equal(lens_mt, torch.clamp(lens - T, min=0).to(torch.int32) + T))
+        multi = {"tokens": T, "us_per_token": round(e0.elapsed_time(e1) * 1e3 / T, 1),
+                 "start_lengths": "each batch row T rows short of its length", "lengths_grew_by_tokens": ok}
+        log(f"multi-token decode: {multi['us_per_token']} us per token (append + step)")
+
     # Roofline of the attention kernel with the largest share of the step.
     attn_keys = [kk for kk in layer_bytes if kk in kernels]
     dom = max(attn_keys, key=lambda kk: kernels[kk]["us_per_step"])
@@ -325,6 +350,7 @@ def main():
         "step_us_with_launch_timing": round(instrumented_us, 1),
         "selection_overhead_frac": round(sel_us / (ms_per_step * 1e3), 4),
         "comparison_schedules": comparison or None,
+        "multi_token_decode": multi,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

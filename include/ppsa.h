@@ -146,6 +146,26 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Append one decode token to the caches (section 2, problem definition:
+ * decoding produces one token at a time and each token's K and V rows join
+ * the cache before the next attention). For every batch row b with
+ * n = seq_lens[b] clamped into [0, Nmax]: when n < Nmax, k_new[l,b,h,:] and
+ * v_new[l,b,h,:] are stored at row n of k_cache[l,b,h] and v_cache[l,b,h]
+ * for every layer l < num_layers and KV head h, and seq_lens[b] becomes
+ * n + 1; when n = Nmax (full) nothing is stored and seq_lens[b] becomes
+ * Nmax.
+ *   k_new, v_new:  [L, B, Hkv, d], element type `dtype`
+ *   k/v_cache:     [L, B, Hkv, Nmax, d], written at one row per (l, b, h)
+ *   seq_lens:      [B] int32, read and written on the device
+ * One kernel on `stream`: a ppsa_decode_step enqueued after it on the same
+ * stream sees the new rows and lengths. A multi-token decode calls this,
+ * then ppsa_decode_step, once per token. Pointers must be 16-byte aligned
+ * (seq_lens 4-byte); errors as for the other entry points.
+ */
+int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, int32_t* seq_lens, void* stream);
+
+/*
  * Launch timing (instrumentation; not part of the method). While timing is
  * on, every kernel the entry points above enqueue is bracketed by two HIP
  * events recorded on the same stream, and ppsa_timing_read() returns, per
@@ -173,7 +193,8 @@ typedef enum ppsa_kernel_kind {
   PPSA_KERNEL_ATTN_SPARSE = 2,      /* split attention pass over selected rows */
   PPSA_KERNEL_COMBINE = 3,          /* merge of split partials */
   PPSA_KERNEL_SELECT = 4,           /* top-k selection */
-  PPSA_KERNEL_KINDS = 5
+  PPSA_KERNEL_APPEND = 5,           /* append of a token's K/V rows */
+  PPSA_KERNEL_KINDS = 6
 } ppsa_kernel_kind;
 
 int ppsa_timing_enable(int32_t capacity);

@@ -21,6 +21,8 @@ with Position Persistent Sparse Attention" (arXiv 2410.05076).
         only reading that type-checks.
   [S3P] section 3, PPSA paragraph: later layers reuse the token set of the
         preceding selection layer instead of selecting per layer and head.
+  [S2D] section 2 "Core idea", problem definition: decoding produces one
+        token at a time against a KV cache that grows with every token.
 
 Readings where the page is silent (each repeated in the design notes):
   R-score  the selection ranks positions by the raw logit q.k/sqrt(d); for a
@@ -38,6 +40,10 @@ Readings where the page is silent (each repeated in the design notes):
   R-multi  a sparse index list is taken as given: entries outside [0, N_b)
            are skipped, a repeated entry counts once per occurrence.
   R-lens   a length outside [0, Nmax] is clamped into it.
+  R-append a decode step first stores the new token's K and V rows at
+           position N_b of every layer and KV head, and N_b becomes N_b + 1;
+           the step's attention then sees them. A full cache (N_b = Nmax)
+           takes no row and keeps N_b = Nmax.
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py
 against brute force, closed forms, invariants and a library routine (torch
@@ -173,3 +179,43 @@ def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, 
             sels.append(selection)
     return np.stack(outs), sels
 
+
+
+def append_kv(K_layers, V_layers, seq_lens, k_new, v_new):
+    """Store one new token's rows and grow the lengths [S2D] (R-append, R-lens).
+
+    K_layers / V_layers: per-layer storage arrays [B, Hkv, Nmax, d], updated
+    in place; k_new / v_new [L, B, Hkv, d] in the same storage type.
+    Returns the new lengths (int64 [B]).
+    """
+    n_max = K_layers[0].shape[2]
+    new_lens = np.empty(len(seq_lens), dtype=np.int64)
+    for b, n in enumerate(seq_lens):
+        n = min(max(int(n), 0), n_max)
+        if n == n_max:
+            new_lens[b] = n_max
+            continue
+        for layer in range(len(K_layers)):
+            K_layers[layer][b, :, n, :] = k_new[layer, b]
+            V_layers[layer][b, :, n, :] = v_new[layer, b]
+        new_lens[b] = n + 1
+    return new_lens
+
+
+def decode_steps(schedule, q_steps, K_layers, V_layers, seq_lens, k_new_steps, v_new_steps, group: int, topk: int,
+                 scale: float, dtype: str):
+    """T decode steps, each appending its token's rows before its layers run [S2D].
+
+    q_steps [T, L, B, Hq, d]; k_new_steps / v_new_steps [T, L, B, Hkv, d];
+    K_layers / V_layers as in append_kv (updated in place).
+    Returns (outs [T, L, B, Hq, d], selections per step, final lengths).
+    """
+    lens = np.asarray(seq_lens)
+    outs, sels = [], []
+    for t in range(len(q_steps)):
+        lens = append_kv(K_layers, V_layers, lens, k_new_steps[t], v_new_steps[t])
+        out, sel = decode_step(schedule, q_steps[t], lambda layer: (K_layers[layer], V_layers[layer]), lens,
+                               group, topk, scale, dtype)
+        outs.append(out)
+        sels.append(sel)
+    return np.stack(outs), sels, lens

@@ -25,8 +25,8 @@ PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
-PPSA_KERNEL_KINDS = 5
-KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select")  # ppsa_kernel_kind order
+PPSA_KERNEL_KINDS = 6
+KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select", "append")  # ppsa_kernel_kind order
 
 
 class Dims(ctypes.Structure):
@@ -57,12 +57,13 @@ def _load():
     lib.ppsa_select_topk.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
     lib.ppsa_timing_enable.argtypes = [i32]
     lib.ppsa_timing_read.argtypes = [vp, vp, i32, vp]
     lib.ppsa_timing_kernel_name.argtypes = [i32]
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
-                 "ppsa_decode_step", "ppsa_timing_enable", "ppsa_timing_read"):
+                 "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -205,6 +206,24 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
                                  _ptr(seq_lens), int(topk), _ptr(out), _ptr(idx), _ptr(scores), _ptr(ws),
                                  ws.numel(), _stream(q.device)), "ppsa_decode_step")
     return out, idx
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, seq_lens):
+    """Append one token: k_new/v_new [L,B,Hkv,d] go to row seq_lens[b] of the caches [L,B,Hkv,Nmax,d];
+    seq_lens (device int32) grows by one per batch row with room."""
+    _require(k_cache.dim() == 5 and v_cache.shape == k_cache.shape, "k_cache/v_cache must be [L,B,Hkv,Nmax,d]")
+    L, B, Hkv, n_max, d = k_cache.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _require(tuple(t.shape) == (L, B, Hkv, d), f"{name} must be [L,B,Hkv,d] = {(L, B, Hkv, d)}")
+        _require(t.dtype == k_cache.dtype and t.is_contiguous() and t.device == k_cache.device,
+                 f"{name}: dtype/device/layout must match the cache")
+    _require(v_cache.dtype == k_cache.dtype and k_cache.is_contiguous() and v_cache.is_contiguous(),
+             "caches must be contiguous with one dtype")
+    _require(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,) and seq_lens.device == k_cache.device,
+             "seq_lens must be int32 [B] on the cache's device")
+    dims = make_dims(B, Hkv, Hkv, d, n_max, k_cache.dtype)
+    _check(_lib.ppsa_append_kv(ctypes.byref(dims), L, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(seq_lens), _stream(k_cache.device)), "ppsa_append_kv")
 
 
 def timing_enable(capacity: int):

@@ -308,6 +308,32 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
   return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out);
 }
 
+int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, int32_t* seq_lens, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if (num_layers < 0) return PPSA_ERR_INVALID_ARG;
+  if (dims->batch == 0 || num_layers == 0) return PPSA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return PPSA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(seq_lens, 4))
+    return PPSA_ERR_INVALID_ARG;
+  AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.seq_lens = seq_lens;
+  a.layers = num_layers;
+  a.batch = dims->batch;
+  a.kv_heads = dims->num_kv_heads;
+  a.max_len = dims->max_seq_len;
+  a.row_bytes = dims->head_dim * (int)elem_bytes(dims->dtype);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return finish(timed(KERNEL_APPEND, st, [&] { return launch_append(a, st); }));
+}
+
 int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {

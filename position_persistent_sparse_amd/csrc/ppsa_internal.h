@@ -71,7 +71,19 @@ constexpr int kMaxGroup = 16;
 // Most splits one unit may be cut into (the merge pass keeps one weight per split in LDS).
 constexpr int kMaxSplitsPerUnit = 256;
 
+// Append of one token's K/V rows (append.hip): rows [L, B, Hkv] of row_bytes each go to position
+// seq_lens[b] of the caches [L, B, Hkv, max_len]; seq_lens[b] then grows by one (capped at max_len).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  int32_t* seq_lens;
+  int32_t layers, batch, kv_heads, max_len, row_bytes;
+};
+
 hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
@@ -82,7 +94,8 @@ enum KernelKind : int {
   KERNEL_ATTN_SPARSE = 2,
   KERNEL_COMBINE = 3,
   KERNEL_SELECT = 4,
-  KERNEL_KINDS = 5
+  KERNEL_APPEND = 5,
+  KERNEL_KINDS = 6
 };
 // Records a begin event on `stream` when timing is on; returns a token (-1: untimed) and the end event.
 int timing_begin(hipStream_t stream, hipEvent_t* end);

@@ -142,13 +142,33 @@ def test_timing_api_without_gpu_work():
     res = ppsa.timing_read()
     assert res["dropped"] == 0
     assert all(res[k] == (0, 0.0) for k in ppsa.KERNEL_KEYS)
-    counts = (ctypes.c_int32 * 5)()
-    ms = (ctypes.c_double * 5)()
-    assert LIB.ppsa_timing_read(counts, ms, 4, None) == ppsa.PPSA_ERR_INVALID_ARG
-    assert LIB.ppsa_timing_read(None, ms, 5, None) == ppsa.PPSA_ERR_INVALID_ARG
-    assert LIB.ppsa_timing_read(counts, None, 5, None) == ppsa.PPSA_ERR_INVALID_ARG
-    assert LIB.ppsa_timing_read(counts, ms, 5, None) == ppsa.PPSA_OK
+    nk = ppsa.PPSA_KERNEL_KINDS
+    assert nk == len(ppsa.KERNEL_KEYS) == 6
+    counts = (ctypes.c_int32 * nk)()
+    ms = (ctypes.c_double * nk)()
+    assert LIB.ppsa_timing_read(counts, ms, nk - 1, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(None, ms, nk, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(counts, None, nk, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_timing_read(counts, ms, nk, None) == ppsa.PPSA_OK
     names = [ppsa.timing_kernel_name(i) for i in range(ppsa.PPSA_KERNEL_KINDS)]
     assert len(set(names)) == ppsa.PPSA_KERNEL_KINDS and "unknown" not in names
     assert ppsa.timing_kernel_name(ppsa.PPSA_KERNEL_KINDS) == "unknown"
     assert ppsa.timing_kernel_name(-1) == "unknown"
+
+
+def append(d, layers=2, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE):
+    return LIB.ppsa_append_kv(ctypes.byref(d), layers, kn, vn, kc, vc, lens, None)
+
+
+def test_append_kv_validation():
+    d = dims()
+    assert append(d, layers=-1) == ppsa.PPSA_ERR_INVALID_ARG
+    assert append(d, layers=0) == ppsa.PPSA_OK                       # nothing to do, nothing launched
+    assert append(dims(batch=0)) == ppsa.PPSA_OK
+    for kw in ("kn", "vn", "kc", "vc", "lens"):
+        assert append(d, **{kw: None}) == ppsa.PPSA_ERR_INVALID_ARG, kw
+    for kw in ("kn", "vn", "kc", "vc"):
+        assert append(d, **{kw: ODD}) == ppsa.PPSA_ERR_INVALID_ARG, kw
+    assert append(d, lens=ctypes.c_void_p(0x100002)) == ppsa.PPSA_ERR_INVALID_ARG
+    assert append(dims(head_dim=96)) == ppsa.PPSA_ERR_UNSUPPORTED
+    assert append(dims(batch=-1)) == ppsa.PPSA_ERR_INVALID_ARG

@@ -7,7 +7,9 @@ Kinds of pin (none re-types the oracle's own formula):
   - closed forms: q = 0 (uniform weights), one row, two rows (logistic
     weights), one dominant key, exact bf16 bit patterns;
   - invariants: softmax rows sum to one, PPSA with k = N equals full
-    attention, the sparse output ignores the order of the index list.
+    attention, the sparse output ignores the order of the index list;
+  - multi-step decode against attention over a cache built by concatenating
+    the new tokens' rows, and a dominant new key that must be selected.
 The mutation test at the bottom plants plausible mistakes in the oracle and
 checks that at least one pin fails for each.
 """
@@ -247,11 +249,67 @@ def pin_empty_and_short():
     assert list(O.select_topk(s, 5)) == [2, 0, 1, -1, -1]
 
 
+def _multistep_case(schedule, topk=3):
+    L, B, Hkv, g, d, n_max, T = len(schedule), 2, 2, 2, 8, 10, 3
+    lens0 = np.array([6, 9])
+    K = [RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32) for _ in range(L)]
+    V = [RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32) for _ in range(L)]
+    q = RNG.standard_normal((T, L, B, Hkv * g, d)).astype(np.float32)
+    kn = RNG.standard_normal((T, L, B, Hkv, d)).astype(np.float32)
+    vn = RNG.standard_normal((T, L, B, Hkv, d)).astype(np.float32)
+    K0, V0 = [x.copy() for x in K], [x.copy() for x in V]
+    outs, sels, lens = O.decode_steps(schedule, q, K, V, lens0, kn, vn, g, topk, 0.35, "f32")
+    return (L, B, Hkv, g, d, n_max, T, lens0, K0, V0, q, kn, vn), outs, sels, lens
+
+
+def pin_multistep_full_vs_torch_sdpa_on_concatenated_cache():
+    """T full-attention steps with appends equal attention over the original rows followed by the new
+    tokens' rows, built by concatenation (a cache that fills up stops taking rows)."""
+    (L, B, Hkv, g, d, n_max, T, lens0, K0, V0, q, kn, vn), outs, _, lens = _multistep_case(["F", "F"])
+    for b in range(B):
+        taken = min(T, n_max - int(lens0[b]))
+        assert int(lens[b]) == int(lens0[b]) + taken
+        for t in range(T):
+            m = min(t + 1, taken)
+            for layer in range(L):
+                for h in range(Hkv):
+                    Kc = np.concatenate([K0[layer][b, h, :lens0[b]], kn[:m, layer, b, h]])
+                    Vc = np.concatenate([V0[layer][b, h, :lens0[b]], vn[:m, layer, b, h]])
+                    want = torch_attention(q[t, layer, b, h * g:(h + 1) * g], Kc, Vc, 0.35)
+                    np.testing.assert_allclose(outs[t, layer, b, h * g:(h + 1) * g], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_multistep_new_dominant_key_is_selected():
+    """A new token whose key dominates every query is the single selected position at its step."""
+    L, B, Hkv, g, d, n_max = 3, 1, 1, 2, 4, 12
+    K = [RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32) for _ in range(L)]
+    V = [RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32) for _ in range(L)]
+    q = np.ones((2, L, B, g, d), dtype=np.float32)
+    kn = np.zeros((2, L, B, Hkv, d), dtype=np.float32)
+    kn[1] = 50.0  # step 1's token dominates; step 0's token has logit 0
+    vn = RNG.standard_normal((2, L, B, Hkv, d)).astype(np.float32)
+    _, sels, lens = O.decode_steps(["F", "F", "X"], q, K, V, np.array([7]), kn, vn, g, 1, 0.5, "f32")
+    assert int(lens[0]) == 9
+    assert as_set(sels[1][0][0, 0]) == [8]
+
+
+def pin_append_into_full_cache_changes_nothing():
+    K = [RNG.standard_normal((1, 2, 5, 4)).astype(np.float32)]
+    V = [RNG.standard_normal((1, 2, 5, 4)).astype(np.float32)]
+    K0, V0 = K[0].copy(), V[0].copy()
+    lens = O.append_kv(K, V, np.array([5]), np.ones((1, 1, 2, 4), np.float32), np.ones((1, 1, 2, 4), np.float32))
+    assert int(lens[0]) == 5
+    np.testing.assert_array_equal(K[0], K0)
+    np.testing.assert_array_equal(V[0], V0)
+
+
 PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets, pin_select_vs_torch_sort,
         pin_q_zero_selects_prefix, pin_full_vs_torch_sdpa, pin_q_zero_mean, pin_single_row,
         pin_two_rows_closed_form, pin_dominant_key, pin_softmax_rows_sum_to_one, pin_group_score_is_sum_of_heads,
         pin_sparse_equals_full_when_k_is_n, pin_sparse_permutation_invariant,
-        pin_sparse_skips_invalid_and_counts_repeats, pin_reuse_most_recent_selection, pin_empty_and_short]
+        pin_sparse_skips_invalid_and_counts_repeats, pin_reuse_most_recent_selection, pin_empty_and_short,
+        pin_multistep_full_vs_torch_sdpa_on_concatenated_cache, pin_multistep_new_dominant_key_is_selected,
+        pin_append_into_full_cache_changes_nothing]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -302,6 +360,25 @@ def _mut_first_selection(kind, q, K, V, seq_lens, group, topk, scale, dtype, sel
     return out, sel, sc
 
 
+def _mut_append_over_last_row(K_layers, V_layers, seq_lens, k_new, v_new):
+    n_max = K_layers[0].shape[2]
+    lens = np.array([min(max(int(n), 0), n_max) for n in seq_lens])
+    for b, n in enumerate(lens):
+        if 0 < n < n_max:
+            for layer in range(len(K_layers)):
+                K_layers[layer][b, :, n - 1, :] = k_new[layer, b]
+                V_layers[layer][b, :, n - 1, :] = v_new[layer, b]
+    return np.minimum(lens + 1, n_max)
+
+
+_orig_append = O.append_kv
+
+
+def _mut_append_without_growth(K_layers, V_layers, seq_lens, k_new, v_new):
+    _orig_append(K_layers, V_layers, seq_lens, k_new, v_new)
+    return np.asarray(seq_lens, dtype=np.int64)
+
+
 MUTANTS = {
     "drop_scale": ("logits", _mut_no_scale),
     "ties_to_higher_index": ("select_topk", _mut_ties_high),
@@ -309,6 +386,8 @@ MUTANTS = {
     "swapped_k_and_v": ("attend", _mut_swapped_kv),
     "no_renormalisation": ("attend", _mut_no_renorm),
     "reuse_first_selection": ("decode_layer", _mut_first_selection),
+    "append_over_last_row": ("append_kv", _mut_append_over_last_row),
+    "append_without_growth": ("append_kv", _mut_append_without_growth),
 }
 
 
