@@ -265,6 +265,23 @@ def main():
         comparison[name] = {"schedule": "".join(sch), "step_us": round(us, 1),
                             "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
         del c_idx
+    if not args.no_comparison and n_sel:
+        # Selection variant: one set per batch row over all of its query heads (same schedule and inputs).
+        def shared_step():
+            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
+                             select_mode="shared")
+
+        shared_step()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            shared_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        comparison["shared_selection"] = {"schedule": "".join(sched), "select_mode": "shared", "step_us": round(us, 1),
+                                          "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
     if comparison:
         log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
 

@@ -118,6 +118,21 @@ int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* 
                      int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Selection semantics (the page does not fix them; see the header note).
+ * PPSA_SELECT_PER_KV_HEAD (the default everywhere): one set per (batch row,
+ * KV head), ranked by that KV head's scores. PPSA_SELECT_SHARED: one set per
+ * batch row, ranked by the float32 sum over its KV heads of their scores (so
+ * by the sum of the raw logits of every query head), and written to every KV
+ * head's row of idx -- the reading of the section 3 PPSA paragraph in which
+ * the set is shared by all heads rather than chosen per head.
+ */
+typedef enum ppsa_select_mode { PPSA_SELECT_PER_KV_HEAD = 0, PPSA_SELECT_SHARED = 1 } ppsa_select_mode;
+
+/* ppsa_select_topk with a selection mode (an unknown mode returns PPSA_ERR_INVALID_ARG). */
+int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
+                        int32_t select_mode, int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sparse attention over pre-selected positions (the PPSA layer kind, section
  * 3 PPSA paragraph): attention of every query head of KV group kv over the
  * rows idx[b,kv,0..topk) only, renormalised over them. Entries outside
@@ -144,6 +159,13 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
 int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ppsa_decode_step with a selection mode for its PPSA_FULL_SELECT layers (scores are written per KV
+ * head either way; an unknown mode returns PPSA_ERR_INVALID_ARG). */
+int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                        const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+                        int32_t select_mode, void* out, int32_t* idx, float* scores, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * Append one decode token to the caches (section 2, problem definition:

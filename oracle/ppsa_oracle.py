@@ -40,6 +40,10 @@ Readings where the page is silent (each repeated in the design notes):
   R-multi  a sparse index list is taken as given: entries outside [0, N_b)
            are skipped, a repeated entry counts once per occurrence.
   R-lens   a length outside [0, Nmax] is clamped into it.
+  R-shared (selection variant, off by default) one set per batch row,
+           ranked by the float32 rounding of the sum over all of the row's
+           query heads of the raw logit (each head against its own KV head's
+           key at that position) and applied to every KV head.
   R-append a decode step first stores the new token's K and V rows at
            position N_b of every layer and KV head, and N_b becomes N_b + 1;
            the step's attention then sees them. A full cache (N_b = Nmax)
@@ -121,8 +125,17 @@ def sparse_attention(q, K, V, idx, n_live: int, scale: float) -> np.ndarray:
     return attend(q, K[keep], V[keep], scale)
 
 
+def shared_selection_scores(q_all, K_all, n_live: int, group: int, scale: float) -> np.ndarray:
+    """float32 score per live position summed over every query head of a batch row (R-shared).
+    q_all [Hq, d] and K_all [Hkv, N, d] in float64."""
+    total = np.zeros(n_live, dtype=np.float64)
+    for h in range(K_all.shape[0]):
+        total += logits(q_all[h * group:(h + 1) * group], K_all[h, :n_live], scale).sum(axis=0)
+    return total.astype(np.float32)
+
+
 def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: float, dtype: str,
-                 selection=None):
+                 selection=None, select_mode: str = "kv_head"):
     """One layer of the decode step [S2, S3F].
 
     q [B, Hq, d], K and V [B, Hkv, Nmax, d] in storage form; `selection`
@@ -159,10 +172,14 @@ def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: flo
                     s = selection_scores(qg, Kb, n, scale)
                     scores[b, h, :n] = s
                     new_sel[b, h] = select_topk(s, topk)
+        if kind == FULL_SELECT and select_mode == "shared":
+            s = shared_selection_scores(widen(q[b], dtype), widen(K[b, :, :n], dtype), n, group, scale)
+            new_sel[b, :] = select_topk(s, topk)
     return out, new_sel, scores
 
 
-def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, scale: float, dtype: str):
+def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, scale: float, dtype: str,
+                select_mode: str = "kv_head"):
     """Whole decode step: run `schedule` (list of F/X/S) over per-layer inputs.
 
     q_layers[l] is [B, Hq, d]; kv_layers(l) returns (K, V) for layer l.
@@ -173,7 +190,7 @@ def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, 
     for layer, kind in enumerate(schedule):
         K, V = kv_layers(layer)
         out, selection, _ = decode_layer(kind, q_layers[layer], K, V, seq_lens, group, topk, scale, dtype,
-                                         selection)
+                                         selection, select_mode)
         outs.append(out)
         if kind == FULL_SELECT:
             sels.append(selection)

@@ -25,6 +25,8 @@ PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
+PPSA_SELECT_PER_KV_HEAD, PPSA_SELECT_SHARED = 0, 1
+SELECT_MODES = {"kv_head": PPSA_SELECT_PER_KV_HEAD, "shared": PPSA_SELECT_SHARED}
 PPSA_KERNEL_KINDS = 6
 KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select", "append")  # ppsa_kernel_kind order
 
@@ -55,6 +57,8 @@ def _load():
     lib.ppsa_full_attn.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ppsa_full_attn_select.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_select_topk.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
+    lib.ppsa_select_topk_ex.argtypes = [dp, vp, vp, i32, i32, vp, vp, sz, vp]
+    lib.ppsa_decode_step_ex.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
@@ -63,7 +67,8 @@ def _load():
     lib.ppsa_timing_kernel_name.argtypes = [i32]
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
-                 "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read"):
+                 "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read",
+                 "ppsa_select_topk_ex", "ppsa_decode_step_ex"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -158,15 +163,16 @@ def full_attn_select(q, k_cache, v_cache, seq_lens, topk: int, out=None, scores=
     return out, idx
 
 
-def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None):
+def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: str = "kv_head"):
+    """Top-k per (batch row, KV head), or per batch row over the KV heads' summed scores (mode "shared")."""
     _require(scores.dim() == 3 and scores.dtype == torch.float32 and scores.is_contiguous() and scores.is_cuda,
              "scores must be contiguous float32 [B, Hkv, N] on the GPU")
     B, Hkv, N = scores.shape
     dims = make_dims(B, num_q_heads or Hkv, Hkv, 128, N, PPSA_F32)
     if idx is None:
         idx = torch.empty((B, Hkv, int(topk)), dtype=torch.int32, device=scores.device)
-    _check(_lib.ppsa_select_topk(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), int(topk), _ptr(idx), None, 0,
-                                 _stream(scores.device)), "ppsa_select_topk")
+    _check(_lib.ppsa_select_topk_ex(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), int(topk), SELECT_MODES[mode],
+                                    _ptr(idx), None, 0, _stream(scores.device)), "ppsa_select_topk_ex")
     return idx
 
 
@@ -190,7 +196,7 @@ def schedule_codes(schedule) -> ctypes.Array:
 
 
 def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, idx=None, scores=None,
-                workspace=None, scale: float = 0.0, sched_codes=None):
+                workspace=None, scale: float = 0.0, sched_codes=None, select_mode: str = "kv_head"):
     """One decode step; returns (out [L,B,Hq,d], idx [S,B,Hkv,topk]) with S = selection layers."""
     _check_tensors(q, k_cache, v_cache, seq_lens, layered=True)
     dims = _dims_of(q, k_cache, scale, layered=True)
@@ -202,9 +208,9 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
         idx = torch.empty((n_sel, dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
     ws = alloc_workspace(dims, topk if n_sel else 0, q.device) if workspace is None else workspace
     codes = schedule_codes(schedule) if sched_codes is None else sched_codes
-    _check(_lib.ppsa_decode_step(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(seq_lens), int(topk), _ptr(out), _ptr(idx), _ptr(scores), _ptr(ws),
-                                 ws.numel(), _stream(q.device)), "ppsa_decode_step")
+    _check(_lib.ppsa_decode_step_ex(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(seq_lens), int(topk), SELECT_MODES[select_mode], _ptr(out), _ptr(idx),
+                                    _ptr(scores), _ptr(ws), ws.numel(), _stream(q.device)), "ppsa_decode_step_ex")
     return out, idx
 
 

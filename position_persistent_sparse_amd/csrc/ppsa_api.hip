@@ -166,8 +166,9 @@ int run_combine(const Ctx& c, int splits, void* out) {
   return finish(timed(KERNEL_COMBINE, c.stream, [&] { return launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream); }));
 }
 
-int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx) {
+int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx, int mode) {
   SelectArgs s{};
+  s.shared = mode == PPSA_SELECT_SHARED ? 1 : 0;
   s.scores = scores;
   s.seq_lens = seq_lens;
   s.idx = idx;
@@ -179,7 +180,7 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
 }
 
 int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
-             int topk, float* scores, int32_t* idx) {
+             int topk, float* scores, int32_t* idx, int select_mode) {
   AttnArgs a = base_args(c, q, k, v, seq_lens, out);
   a.splits = c.plan.full_splits;
   a.rows_per_split = c.plan.full_rows;
@@ -191,7 +192,7 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
   }));
   if (rc == PPSA_OK) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
-  return run_select(c, a.scores, seq_lens, topk, idx);
+  return run_select(c, a.scores, seq_lens, topk, idx, select_mode);
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
@@ -259,7 +260,7 @@ int ppsa_full_attn(const ppsa_dims* dims, const void* q, const void* k_cache, co
   if (!c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return run_full(c, q, k_cache, v_cache, seq_lens, out, 0, nullptr, nullptr);
+  return run_full(c, q, k_cache, v_cache, seq_lens, out, 0, nullptr, nullptr, PPSA_SELECT_PER_KV_HEAD);
 }
 
 int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
@@ -275,11 +276,18 @@ int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_ca
   if (!c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return run_full(c, q, k_cache, v_cache, seq_lens, out, topk, scores, idx);
+  return run_full(c, q, k_cache, v_cache, seq_lens, out, topk, scores, idx, PPSA_SELECT_PER_KV_HEAD);
 }
 
 int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
                      int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  return ppsa_select_topk_ex(dims, scores, seq_lens, topk, PPSA_SELECT_PER_KV_HEAD, idx, workspace, workspace_bytes,
+                             stream);
+}
+
+int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
+                        int32_t select_mode, int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED) return PPSA_ERR_INVALID_ARG;
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
@@ -289,7 +297,7 @@ int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* 
   if (workspace_bytes > 0 && !workspace) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
   (void)hipGetLastError();
-  return run_select(c, scores, seq_lens, topk, idx);
+  return run_select(c, scores, seq_lens, topk, idx, select_mode);
 }
 
 int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
@@ -337,6 +345,15 @@ int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new,
 int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return ppsa_decode_step_ex(dims, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, PPSA_SELECT_PER_KV_HEAD,
+                             out, idx, scores, workspace, workspace_bytes, stream);
+}
+
+int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                        const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+                        int32_t select_mode, void* out, int32_t* idx, float* scores, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED) return PPSA_ERR_INVALID_ARG;
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if (num_layers < 0 || (num_layers > 0 && !schedule)) return PPSA_ERR_INVALID_ARG;
@@ -376,12 +393,12 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
     char* ol = static_cast<char*>(out) + l * q_layer;
     switch (schedule[l]) {
       case PPSA_FULL:
-        rc = run_full(c, ql, kl, vl, seq_lens, ol, 0, nullptr, nullptr);
+        rc = run_full(c, ql, kl, vl, seq_lens, ol, 0, nullptr, nullptr, select_mode);
         break;
       case PPSA_FULL_SELECT:
         ++sel;
         rc = run_full(c, ql, kl, vl, seq_lens, ol, topk, scores ? scores + sel * score_slot : nullptr,
-                      idx + sel * idx_slot);
+                      idx + sel * idx_slot, select_mode);
         break;
       default:
         rc = run_sparse(c, ql, kl, vl, seq_lens, idx + sel * idx_slot, topk, ol);

@@ -52,6 +52,7 @@ struct SelectArgs {
   const int32_t* seq_lens;  // [B]
   int32_t* idx;             // [B, Hkv, topk]
   int32_t batch, kv_heads, max_len, topk;
+  int32_t shared;           // 1: one set per batch row over the sum of its KV heads' scores
 };
 
 // Vector-ALU attention pass (any supported dtype / head_dim / group).

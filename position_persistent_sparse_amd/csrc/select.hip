@@ -80,7 +80,9 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
   return r;
 }
 
-template <bool CACHED>
+// SHARED: one set per batch row, ranked by the sum of its KV heads' scores and written to every KV
+// head's row of idx (the head-shared selection variant); otherwise one set per (batch row, KV head).
+template <bool CACHED, bool SHARED>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
   __shared__ uint32_t scan_lds[kWaves + 1];
@@ -88,14 +90,19 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   __shared__ uint32_t s_digit, s_above, s_ncand;
 
   const int unit = blockIdx.x, tid = threadIdx.x;
-  const int b = unit / a.kv_heads;
+  const int b = SHARED ? unit : unit / a.kv_heads;
   const int n = min(max(a.seq_lens[b], 0), a.max_len);
   const int k_eff = min(a.topk, n);
-  const float* s = a.scores + (size_t)unit * a.max_len;
-  int32_t* out = a.idx + (size_t)unit * a.topk;
+  // Score rows summed per position (all KV heads of the batch row when SHARED) and idx rows written.
+  const int rows = SHARED ? a.kv_heads : 1;
+  const float* s = a.scores + (size_t)unit * rows * a.max_len;
+  int32_t* out = a.idx + (size_t)unit * rows * a.topk;
+  auto emit = [&](uint32_t slot, int32_t pos) {
+    for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = pos;
+  };
 
   if (k_eff == n) {  // every live position is kept (includes n == 0)
-    for (int i = tid; i < a.topk; i += kThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < a.topk; i += kThreads) emit(i, i < n ? i : -1);
     return;
   }
 
@@ -119,7 +126,14 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
 #pragma unroll
       for (int j = 0; j < kCached / 4; ++j)
         if (4 * j < per) {
-          const float4 f = *reinterpret_cast<const float4*>(s + p0 + 4 * j);
+          float4 f = *reinterpret_cast<const float4*>(s + p0 + 4 * j);
+          for (int r = 1; r < rows; ++r) {  // heads in order: the same float32 sum every time
+            const float4 g = *reinterpret_cast<const float4*>(s + (size_t)r * a.max_len + p0 + 4 * j);
+            f.x += g.x;
+            f.y += g.y;
+            f.z += g.z;
+            f.w += g.w;
+          }
           k[4 * j] = order_key(f.x);
           k[4 * j + 1] = order_key(f.y);
           k[4 * j + 2] = order_key(f.z);
@@ -128,7 +142,14 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < kCached; ++i)
-        if (i < per) k[i] = i < cnt ? order_key(s[p0 + i]) : 0u;
+        if (i < per) {
+          float f = 0.0f;
+          if (i < cnt) {
+            f = s[p0 + i];
+            for (int r = 1; r < rows; ++r) f += s[(size_t)r * a.max_len + p0 + i];
+          }
+          k[i] = i < cnt ? order_key(f) : 0u;
+        }
     }
     return Span{p0, per, live};
   };
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
     uint32_t take = gtm | lowest_bits(eqm, min(room, n_eq));
     uint32_t slot = gt_before + (needed_eq - room);              // + min(eq_before, needed_eq)
     while (take) {
-      out[slot++] = sp.p0 + __ffs(take) - 1;
+      emit(slot++, sp.p0 + __ffs(take) - 1);
       take &= take - 1u;
     }
     gt_seen += tot_gt;
@@ -238,9 +259,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
-  const dim3 grid(a.batch * a.kv_heads), block(kThreads);
-  if (a.max_len <= kPerSuper) select_topk_kernel<true><<<grid, block, 0, stream>>>(a);
-  else select_topk_kernel<false><<<grid, block, 0, stream>>>(a);
+  const dim3 grid(a.shared ? a.batch : a.batch * a.kv_heads), block(kThreads);
+  const bool cached = a.max_len <= kPerSuper;
+  if (a.shared) {
+    if (cached) select_topk_kernel<true, true><<<grid, block, 0, stream>>>(a);
+    else select_topk_kernel<false, true><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (cached) select_topk_kernel<true, false><<<grid, block, 0, stream>>>(a);
+    else select_topk_kernel<false, false><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

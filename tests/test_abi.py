@@ -172,3 +172,16 @@ def test_append_kv_validation():
     assert append(d, lens=ctypes.c_void_p(0x100002)) == ppsa.PPSA_ERR_INVALID_ARG
     assert append(dims(head_dim=96)) == ppsa.PPSA_ERR_UNSUPPORTED
     assert append(dims(batch=-1)) == ppsa.PPSA_ERR_INVALID_ARG
+
+
+def test_select_mode_validation():
+    d = dims()
+    for mode in (-1, 2, 7):
+        assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, mode, FAKE, None, 0, None) == \
+            ppsa.PPSA_ERR_INVALID_ARG
+        codes = ppsa.schedule_codes("FFX")
+        assert LIB.ppsa_decode_step_ex(ctypes.byref(d), 3, codes, FAKE, FAKE, FAKE, FAKE, 16, mode, FAKE, FAKE, None,
+                                       FAKE, 1 << 30, None) == ppsa.PPSA_ERR_INVALID_ARG
+    # A valid mode reaches the usual checks (idx misaligned for int32 here, so nothing is launched).
+    assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, ppsa.PPSA_SELECT_SHARED,
+                                   ctypes.c_void_p(0x100002), None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG

@@ -303,13 +303,44 @@ def pin_append_into_full_cache_changes_nothing():
     np.testing.assert_array_equal(V[0], V0)
 
 
+def pin_shared_selection_brute_force():
+    """Head-shared selection: the set ranks positions by the sum, over every query head of the batch row,
+    of its logit against its own KV head's key, written out as plain loops; every KV head gets that set."""
+    B, Hkv, g, d, n_max, k, scale = 2, 3, 2, 5, 9, 4, 0.4
+    q = RNG.standard_normal((B, Hkv * g, d)).astype(np.float32)
+    K = RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32)
+    V = RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32)
+    lens = [9, 6]
+    _, sel, _ = O.decode_layer("X", q, K, V, lens, g, k, scale, "f32", None, "shared")
+    for b in range(B):
+        total = []
+        for n in range(lens[b]):
+            acc = 0.0
+            for hq in range(Hkv * g):
+                acc += sum(float(q[b, hq, i]) * float(K[b, hq // g, n, i]) for i in range(d)) * scale
+            total.append(np.float32(acc))
+        want = rank_select(total, k)
+        for h in range(Hkv):
+            assert as_set(sel[b, h]) == want, (b, h)
+
+
+def pin_shared_equals_per_head_with_one_kv_head():
+    q = RNG.standard_normal((2, 4, 6)).astype(np.float32)
+    K = RNG.standard_normal((2, 1, 11, 6)).astype(np.float32)
+    V = RNG.standard_normal((2, 1, 11, 6)).astype(np.float32)
+    _, a, _ = O.decode_layer("X", q, K, V, [11, 8], 4, 5, 0.3, "f32", None, "kv_head")
+    _, b, _ = O.decode_layer("X", q, K, V, [11, 8], 4, 5, 0.3, "f32", None, "shared")
+    np.testing.assert_array_equal(a, b)
+
+
 PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets, pin_select_vs_torch_sort,
         pin_q_zero_selects_prefix, pin_full_vs_torch_sdpa, pin_q_zero_mean, pin_single_row,
         pin_two_rows_closed_form, pin_dominant_key, pin_softmax_rows_sum_to_one, pin_group_score_is_sum_of_heads,
         pin_sparse_equals_full_when_k_is_n, pin_sparse_permutation_invariant,
         pin_sparse_skips_invalid_and_counts_repeats, pin_reuse_most_recent_selection, pin_empty_and_short,
         pin_multistep_full_vs_torch_sdpa_on_concatenated_cache, pin_multistep_new_dominant_key_is_selected,
-        pin_append_into_full_cache_changes_nothing]
+        pin_append_into_full_cache_changes_nothing, pin_shared_selection_brute_force,
+        pin_shared_equals_per_head_with_one_kv_head]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -353,8 +384,8 @@ def _mut_no_renorm(q, K, V, scale):
 _orig_decode_layer = O.decode_layer
 
 
-def _mut_first_selection(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection=None):
-    out, sel, sc = _orig_decode_layer(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection)
+def _mut_first_selection(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection=None, select_mode="kv_head"):
+    out, sel, sc = _orig_decode_layer(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection, select_mode)
     if kind == "X" and selection is not None:
         sel = selection  # keeps reusing the first set
     return out, sel, sc
@@ -379,6 +410,10 @@ def _mut_append_without_growth(K_layers, V_layers, seq_lens, k_new, v_new):
     return np.asarray(seq_lens, dtype=np.int64)
 
 
+def _mut_shared_first_head(q_all, K_all, n_live, group, scale):
+    return O.logits(q_all[:group], K_all[0, :n_live], scale).sum(axis=0).astype(np.float32)
+
+
 MUTANTS = {
     "drop_scale": ("logits", _mut_no_scale),
     "ties_to_higher_index": ("select_topk", _mut_ties_high),
@@ -388,6 +423,7 @@ MUTANTS = {
     "reuse_first_selection": ("decode_layer", _mut_first_selection),
     "append_over_last_row": ("append_kv", _mut_append_over_last_row),
     "append_without_growth": ("append_kv", _mut_append_without_growth),
+    "shared_score_of_first_head_only": ("shared_selection_scores", _mut_shared_first_head),
 }
 
 

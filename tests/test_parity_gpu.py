@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import compare
 import position_persistent_sparse_amd as ppsa
 import synth
 from synth import torch_io
@@ -295,3 +296,61 @@ def test_selection_layer_at_score_staging_cap_sampled():
     n_min = int(gen.seq_lens.min())
     assert np.all(np.isfinite(sc_h[0, :, :, :n_min])), "a live score was not written"
     say("[parity] score-cap: ok")
+
+
+@pytest.mark.parametrize("name", ["llama3-8b-gqa-32k", "llama3-70b-ragged-10k"])
+def test_decode_step_shared_selection(name):
+    """Head-shared selection (one set per batch row over the sum of all query heads' logits): the set is
+    checked with the band rule against the oracle's shared scores and is the same for every KV head;
+    outputs are checked layer by layer, sparse layers against the GPU's own set."""
+    wl = REDUCED[name]
+    gen = synth.Generator(wl)
+    say(f"[parity] shared selection {name}: lens={gen.seq_lens.tolist()}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, select_mode="shared")
+    torch.cuda.synchronize()
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h = idx.cpu().numpy()
+    scale = oracle.default_scale(wl.head_dim)
+    sel = -1
+    for layer, kind in enumerate(wl.schedule()):
+        qh, kh, vh = host[layer]
+        if kind == "X":
+            sel += 1
+            check_layer("F", wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None, None,
+                        f"shared {name} layer {layer} (X output)")
+            for b in range(wl.batch):
+                n = min(max(int(gen.seq_lens[b]), 0), wl.max_len)
+                s = oracle.shared_selection_scores(oracle.widen(qh[b], wl.dtype), oracle.widen(kh[b, :, :n], wl.dtype),
+                                                   n, wl.group, scale)
+                ok, msg, _ = compare.check_selection_band(idx_h[sel, b, 0], s, n, wl.topk)
+                assert ok, f"shared {name} layer {layer} b={b}: {msg}"
+                for h in range(1, wl.kv_heads):
+                    assert np.array_equal(idx_h[sel, b, h], idx_h[sel, b, 0]), (layer, b, h)
+        else:
+            check_layer(kind, wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None,
+                        idx_h[sel] if sel >= 0 else None, f"shared {name} layer {layer} ({kind})")
+    say(f"[parity] shared selection {name}: ok")
+
+
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_select_topk_shared_exact(n):
+    """The head-shared select ranks the float32 sum of the KV heads' scores, added in head order; the same
+    sum formed in numpy gives the exact expected set (ties included)."""
+    rng = np.random.default_rng(n + 1)
+    B, H = 3, 4
+    s = rng.choice(np.array([-1.0, 0.0, 0.25, 0.5, 1.5], dtype=np.float32), size=(B, H, n))
+    s[1] = (rng.standard_normal((H, n)) * 2).astype(np.float32)
+    lens = np.array([n, n - 77, 1000], dtype=np.int32)
+    tot = s[:, 0].copy()
+    for h in range(1, H):
+        tot = (tot + s[:, h]).astype(np.float32)
+    for k in (1, 500, 2999):
+        idx = ppsa.select_topk(torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV), k, mode="shared")
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for b in range(B):
+            m = int(lens[b])
+            want = oracle.select_topk(tot[b, :m], k)
+            for h in range(H):
+                assert np.array_equal(got[b, h], np.sort(want[want >= 0]).tolist() + [-1] * (k - min(k, m))), (n, k, b, h)
