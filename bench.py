@@ -265,7 +265,22 @@ def main():
         comparison[name] = {"schedule": "".join(sch), "step_us": round(us, 1),
                             "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
         del c_idx
+    def overlap(a, b):
+        """Mean over (selection layer, batch row, KV head) of the fraction of set a also in set b."""
+        fr = []
+        for sel_i in range(a.shape[0]):
+            for bb in range(a.shape[1]):
+                for hh in range(a.shape[2]):
+                    x, y = a[sel_i, bb, hh], b[sel_i, bb, hh]
+                    x = x[x >= 0]
+                    if x.numel():
+                        fr.append(float(torch.isin(x, y[y >= 0]).float().mean()))
+        return round(sum(fr) / max(len(fr), 1), 4)
+
     if not args.no_comparison and n_sel:
+        step()
+        torch.cuda.synchronize()
+        idx_default = idx.clone()
         # Selection variant: one set per batch row over all of its query heads (same schedule and inputs).
         def shared_step():
             ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
@@ -281,7 +296,25 @@ def main():
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         comparison["shared_selection"] = {"schedule": "".join(sched), "select_mode": "shared", "step_us": round(us, 1),
-                                          "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
+                                          "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
+                                          "overlap_with_default_set": overlap(idx_default, idx)}
+
+        def softmax_step():
+            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
+                             select_mode="softmax")
+
+        softmax_step()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            softmax_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        comparison["softmax_selection"] = {"schedule": "".join(sched), "select_mode": "softmax",
+                                           "step_us": round(us, 1), "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
+                                           "overlap_with_default_set": overlap(idx_default, idx)}
     if comparison:
         log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
 

@@ -125,10 +125,21 @@ int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* 
  * by the sum of the raw logits of every query head), and written to every KV
  * head's row of idx -- the reading of the section 3 PPSA paragraph in which
  * the set is shared by all heads rather than chosen per head.
+ * PPSA_SELECT_SOFTMAX (decode steps only): one set per (batch row, KV head),
+ * ranked by the float32 sum over the group's query heads of the softmax
+ * weight each gives the position (2^(x - M) / L with the head's final max M
+ * and normaliser L of the same full-attention pass); `scores`, when given,
+ * receives these sums. The workspace from ppsa_workspace_bytes(dims, topk)
+ * with topk > 0 covers the head logits this needs.
  */
-typedef enum ppsa_select_mode { PPSA_SELECT_PER_KV_HEAD = 0, PPSA_SELECT_SHARED = 1 } ppsa_select_mode;
+typedef enum ppsa_select_mode {
+  PPSA_SELECT_PER_KV_HEAD = 0,
+  PPSA_SELECT_SHARED = 1,
+  PPSA_SELECT_SOFTMAX = 2
+} ppsa_select_mode;
 
-/* ppsa_select_topk with a selection mode (an unknown mode returns PPSA_ERR_INVALID_ARG). */
+/* ppsa_select_topk with a selection mode (PPSA_SELECT_PER_KV_HEAD or PPSA_SELECT_SHARED; any other
+ * mode returns PPSA_ERR_INVALID_ARG). */
 int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
                         int32_t select_mode, int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -216,7 +227,8 @@ typedef enum ppsa_kernel_kind {
   PPSA_KERNEL_COMBINE = 3,          /* merge of split partials */
   PPSA_KERNEL_SELECT = 4,           /* top-k selection */
   PPSA_KERNEL_APPEND = 5,           /* append of a token's K/V rows */
-  PPSA_KERNEL_KINDS = 6
+  PPSA_KERNEL_SOFTMAX_SCORES = 6,   /* softmax-weight selection scores */
+  PPSA_KERNEL_KINDS = 7
 } ppsa_kernel_kind;
 
 int ppsa_timing_enable(int32_t capacity);

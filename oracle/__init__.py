@@ -6,9 +6,9 @@ import this package. It shares no code with the HIP library.
 from .ppsa_oracle import (FULL, FULL_SELECT, SPARSE, append_kv, attend, decode_layer, decode_step, decode_steps,
                           default_scale,
                           full_attention, logits, select_topk, selection_scores, softmax_weights,
-                          shared_selection_scores, sparse_attention, widen)
+                          shared_selection_scores, softmax_selection_scores, sparse_attention, widen)
 
 __all__ = ["FULL", "FULL_SELECT", "SPARSE", "append_kv", "attend", "decode_layer", "decode_step", "decode_steps",
            "default_scale",
            "full_attention", "logits", "select_topk", "selection_scores", "softmax_weights",
-           "shared_selection_scores", "sparse_attention", "widen"]
+           "shared_selection_scores", "softmax_selection_scores", "sparse_attention", "widen"]

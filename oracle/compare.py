@@ -19,8 +19,8 @@ def live_set(idx) -> list:
     return sorted(int(i) for i in np.asarray(idx).ravel() if i >= 0)
 
 
-def check_selection_band(gpu_idx, oracle_scores, n_live: int, k: int, band: float = 1e-3):
-    """Returns (ok, message, positions inside the band)."""
+def check_selection_band(gpu_idx, oracle_scores, n_live: int, k: int, band: float = 1e-3, rel_band: float = 0.0):
+    """Returns (ok, message, positions inside the band). The band is band + rel_band * |s_k|."""
     gpu_idx = np.asarray(gpu_idx)
     s = np.asarray(oracle_scores, dtype=np.float32)[:n_live].astype(np.float64)
     k_eff = min(k, n_live)
@@ -34,6 +34,7 @@ def check_selection_band(gpu_idx, oracle_scores, n_live: int, k: int, band: floa
     if chosen.min() < 0 or chosen.max() >= n_live:
         return False, "position outside the live range", 0
     sk = np.sort(s)[::-1][k_eff - 1]
+    band = band + rel_band * abs(sk)
     sel = np.zeros(n_live, bool)
     sel[chosen] = True
     must = s > sk + band

@@ -44,6 +44,10 @@ Readings where the page is silent (each repeated in the design notes):
            ranked by the float32 rounding of the sum over all of the row's
            query heads of the raw logit (each head against its own KV head's
            key at that position) and applied to every KV head.
+  R-softmax (selection variant, off by default) one set per (batch row,
+           KV head), ranked by the float32 rounding of the sum over the
+           group's query heads of the softmax weight each head gives the
+           position in this layer's full attention.
   R-append a decode step first stores the new token's K and V rows at
            position N_b of every layer and KV head, and N_b becomes N_b + 1;
            the step's attention then sees them. A full cache (N_b = Nmax)
@@ -134,6 +138,13 @@ def shared_selection_scores(q_all, K_all, n_live: int, group: int, scale: float)
     return total.astype(np.float32)
 
 
+def softmax_selection_scores(q, K, n_live: int, scale: float) -> np.ndarray:
+    """float32 score per live position: sum over the group's query heads of their softmax weights (R-softmax)."""
+    if n_live == 0:
+        return np.zeros(0, dtype=np.float32)
+    return softmax_weights(logits(q, K[:n_live], scale)).sum(axis=0).astype(np.float32)
+
+
 def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: float, dtype: str,
                  selection=None, select_mode: str = "kv_head"):
     """One layer of the decode step [S2, S3F].
@@ -169,7 +180,10 @@ def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: flo
                 Vb = widen(V[b, h, :n], dtype)
                 out[b, heads] = attend(qg, Kb, Vb, scale)
                 if kind == FULL_SELECT:
-                    s = selection_scores(qg, Kb, n, scale)
+                    if select_mode == "softmax":
+                        s = softmax_selection_scores(qg, Kb, n, scale)
+                    else:
+                        s = selection_scores(qg, Kb, n, scale)
                     scores[b, h, :n] = s
                     new_sel[b, h] = select_topk(s, topk)
         if kind == FULL_SELECT and select_mode == "shared":

@@ -25,10 +25,11 @@ PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
-PPSA_SELECT_PER_KV_HEAD, PPSA_SELECT_SHARED = 0, 1
-SELECT_MODES = {"kv_head": PPSA_SELECT_PER_KV_HEAD, "shared": PPSA_SELECT_SHARED}
-PPSA_KERNEL_KINDS = 6
-KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select", "append")  # ppsa_kernel_kind order
+PPSA_SELECT_PER_KV_HEAD, PPSA_SELECT_SHARED, PPSA_SELECT_SOFTMAX = 0, 1, 2
+SELECT_MODES = {"kv_head": PPSA_SELECT_PER_KV_HEAD, "shared": PPSA_SELECT_SHARED, "softmax": PPSA_SELECT_SOFTMAX}
+PPSA_KERNEL_KINDS = 7
+KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select", "append",
+               "softmax_scores")  # ppsa_kernel_kind order
 
 
 class Dims(ctypes.Structure):

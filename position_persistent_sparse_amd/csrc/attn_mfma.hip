@@ -121,6 +121,7 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
 template <int MODE, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int kThreads = WAVES * kWave;
+  constexpr bool kScores = MODE == MODE_FULL_SCORES || MODE == MODE_FULL_HEADS;
   extern __shared__ float dyn[];  // [WAVES][group][kD] wave outputs, then staged sparse positions
   __shared__ float sm_m[WAVES][kMaxGroup];
   __shared__ float sm_l[WAVES][kMaxGroup];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
         s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[blk][c]), qf[c],
                                                          s[blk], 0, 0, 0);
     }
-    if constexpr (MODE == MODE_FULL_SCORES) {
+    if constexpr (kScores) {
       const int tslot = slot0 + ti * kTile;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -203,6 +204,17 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
         x[blk][j] = ((cur.valid >> (4 * blk + j)) & 1u) ? s[blk][j] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, x[blk][j]);
       }
+    if constexpr (MODE == MODE_FULL_HEADS) {
+      // Every query head's logit of the tile's live rows: lane (g, n < group) holds rows 16 blk + 4g + j.
+      if (n < group) {
+        float* hl = a.head_logits + ((size_t)b * a.q_heads + (size_t)kv * group + n) * a.max_len + slot0 + ti * kTile;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((cur.valid >> (4 * blk + j)) & 1u) hl[16 * blk + 4 * g + j] = x[blk][j];
+      }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const bool need = tmax > m_run + kLazyLog2;
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
     }
   }
   __syncthreads();
-  if constexpr (MODE == MODE_FULL_SCORES) {
+  if constexpr (kScores) {
     float* dst = a.scores + unit * (size_t)a.max_len + slot0;
     for (int i = tid; i < slot_end - slot0; i += kThreads) dst[i] = sm_sc[i];
   }
@@ -314,6 +326,7 @@ hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t str
   switch (mode) {
     case MODE_FULL: attn_mfma_kernel<MODE_FULL, WAVES><<<grid, block, lds, stream>>>(a); break;
     case MODE_FULL_SCORES: attn_mfma_kernel<MODE_FULL_SCORES, WAVES><<<grid, block, lds, stream>>>(a); break;
+    case MODE_FULL_HEADS: attn_mfma_kernel<MODE_FULL_HEADS, WAVES><<<grid, block, lds, stream>>>(a); break;
     case MODE_SPARSE: attn_mfma_kernel<MODE_SPARSE, WAVES><<<grid, block, lds, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
@@ -323,7 +336,7 @@ hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t str
 // Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions or scores.
 size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
   size_t lds = (size_t)waves * a.group * kD * sizeof(float);
-  if (mode == MODE_SPARSE || mode == MODE_FULL_SCORES) lds += (size_t)a.rows_per_split * 4;
+  if (mode == MODE_SPARSE || mode == MODE_FULL_SCORES || mode == MODE_FULL_HEADS) lds += (size_t)a.rows_per_split * 4;
   return lds;
 }
 
@@ -332,7 +345,8 @@ size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
 hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream) {
   if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
   if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRowsMfma) return hipErrorInvalidValue;
-  if (mode == MODE_FULL_SCORES && lds_bytes(a, mode, kWaves) > kMaxLdsBytes) return hipErrorInvalidValue;
+  if ((mode == MODE_FULL_SCORES || mode == MODE_FULL_HEADS) && lds_bytes(a, mode, kWaves) > kMaxLdsBytes)
+    return hipErrorInvalidValue;
   // One split per unit means one workgroup per unit: twice the waves keep more rows in flight per CU
   // (measured 8-10 % faster there), while LDS stays within 64 KiB.
   if (a.splits == 1 && lds_bytes(a, mode, kWavesSingle) <= kMaxLdsBytes)

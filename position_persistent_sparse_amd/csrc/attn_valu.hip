@@ -148,6 +148,10 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
           if (h < group) score += dot * a.scale;
         }
         x[u][h] = valid[u] ? dot * a.scale_log2 : NEG_INF;
+        if constexpr (MODE == MODE_FULL_SCORES) {  // softmax-weight variant: every head's logit too
+          if (a.head_logits && valid[u] && part == 0 && h < group)
+            a.head_logits[((size_t)b * a.q_heads + (size_t)kv * group + h) * a.max_len + pos[u]] = x[u][h];
+        }
       }
       if constexpr (MODE == MODE_FULL_SCORES) {
         if (valid[u] && part == 0) a.scores[unit * (size_t)a.max_len + pos[u]] = score;
@@ -277,6 +281,7 @@ int attn_max_sparse_rows() { return kMaxSparseRows; }
 hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hipStream_t stream) {
   if (a.splits <= 0 || a.batch <= 0) return hipSuccess;
   if (mode == MODE_SPARSE && a.rows_per_split > kMaxSparseRows) return hipErrorInvalidValue;
+  if (mode == MODE_FULL_HEADS) mode = MODE_FULL_SCORES;  // the head logits go out when a.head_logits is set
   if (dtype == PPSA_BF16) {
     if (head_dim == 128) return launch_group<uint16_t, 128>(a, mode, stream);
     if (head_dim == 64) return launch_group<uint16_t, 64>(a, mode, stream);

@@ -51,6 +51,7 @@ struct Plan {
   int sparse_rows = 0, sparse_splits = 0;
   int max_splits = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
+  size_t off_heads = 0, off_fm = 0, off_fl = 0;  // softmax-weight selection: head logits, final max / sum
   bool full_ok = true;    // false: full layers would need more splits than one unit may have
   bool sparse_ok = true;  // false: the budget needs more splits than one unit may have
   bool mfma = false;
@@ -105,6 +106,11 @@ Plan make_plan(const ppsa_dims& d, int topk) {
   p.off_o = off; off = align_up(off + heads * p.max_splits * d.head_dim * sizeof(float));
   p.off_scores = off;
   off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * d.max_seq_len * sizeof(float));
+  if (topk > 0) {  // regions of the softmax-weight selection variant
+    p.off_heads = off; off = align_up(off + heads * d.max_seq_len * sizeof(float));
+    p.off_fm = off; off = align_up(off + heads * sizeof(float));
+    p.off_fl = off; off = align_up(off + heads * sizeof(float));
+  }
   p.total = off;
   return p;
 }
@@ -185,14 +191,31 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
   a.splits = c.plan.full_splits;
   a.rows_per_split = c.plan.full_rows;
   const bool select = idx != nullptr;
+  const bool softmax = select && select_mode == PPSA_SELECT_SOFTMAX;
   if (select) a.scores = scores ? scores : reinterpret_cast<float*>(c.ws + c.plan.off_scores);
-  const int mode = select ? MODE_FULL_SCORES : MODE_FULL;
+  if (softmax) a.head_logits = reinterpret_cast<float*>(c.ws + c.plan.off_heads);
+  const int mode = softmax ? MODE_FULL_HEADS : (select ? MODE_FULL_SCORES : MODE_FULL);
   int rc = finish(timed(select ? KERNEL_ATTN_FULL_SCORES : KERNEL_ATTN_FULL, c.stream, [&] {
     return c.plan.mfma ? launch_attn_mfma(a, mode, c.stream) : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream);
   }));
   if (rc == PPSA_OK) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
-  return run_select(c, a.scores, seq_lens, topk, idx, select_mode);
+  if (softmax) {
+    // The scores the selection ranks become the group's softmax-weight sums (written over the logit sums).
+    SoftmaxScoreArgs sa{};
+    sa.head_logits = a.head_logits;
+    sa.stat_m = reinterpret_cast<float*>(c.ws + c.plan.off_fm);
+    sa.stat_l = reinterpret_cast<float*>(c.ws + c.plan.off_fl);
+    sa.seq_lens = seq_lens;
+    sa.scores = a.scores;
+    sa.batch = c.d->batch;
+    sa.q_heads = c.d->num_q_heads;
+    sa.kv_heads = c.d->num_kv_heads;
+    sa.max_len = c.d->max_seq_len;
+    rc = finish(timed(KERNEL_SOFTMAX_SCORES, c.stream, [&] { return launch_softmax_scores(sa, c.stream); }));
+    if (rc != PPSA_OK) return rc;
+  }
+  return run_select(c, a.scores, seq_lens, topk, idx, softmax ? PPSA_SELECT_PER_KV_HEAD : select_mode);
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
@@ -287,6 +310,7 @@ int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* 
 
 int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
                         int32_t select_mode, int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  // PPSA_SELECT_SOFTMAX needs each head's logits, which a score array does not hold.
   if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED) return PPSA_ERR_INVALID_ARG;
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
@@ -353,7 +377,8 @@ int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t
                         const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
                         int32_t select_mode, void* out, int32_t* idx, float* scores, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED) return PPSA_ERR_INVALID_ARG;
+  if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED && select_mode != PPSA_SELECT_SOFTMAX)
+    return PPSA_ERR_INVALID_ARG;
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if (num_layers < 0 || (num_layers > 0 && !schedule)) return PPSA_ERR_INVALID_ARG;

@@ -8,7 +8,9 @@
 
 namespace ppsa {
 
-enum AttnMode : int { MODE_FULL = 0, MODE_FULL_SCORES = 1, MODE_SPARSE = 2 };
+// MODE_FULL_HEADS: full attention writing the group-summed scores and also every query head's
+// logit (log2 units) of every live row, for the softmax-weight selection variant.
+enum AttnMode : int { MODE_FULL = 0, MODE_FULL_SCORES = 1, MODE_SPARSE = 2, MODE_FULL_HEADS = 3 };
 
 // One launch of the split attention pass. Every pointer is a device pointer.
 // The grid is (splits, Hkv, B); split s of unit (b, kv) covers slots
@@ -30,6 +32,7 @@ struct AttnArgs {
   float* part_m;            // [B, Hq, splits]
   float* part_l;            // [B, Hq, splits]
   float* part_o;            // [B, Hq, splits, D]
+  float* head_logits;       // MODE_FULL_HEADS: [B, Hq, max_len], logit * scale * log2(e) per live row
   int32_t batch, q_heads, kv_heads, group, max_len;
   int32_t kslots;           // sparse: entries per unit
   int32_t splits, rows_per_split;
@@ -46,6 +49,18 @@ struct CombineArgs {
   int32_t rows;             // B * Hq
   int32_t splits;           // 1 .. kMaxSplitsPerUnit
 };
+
+// Softmax-weight selection scores (scores.hip): per (b, hq), M = max over live n of head_logits and
+// L = sum 2^(x - M) (stats pass); then scores[b, kv, n] = sum over the group's heads of 2^(x - M) / L.
+struct SoftmaxScoreArgs {
+  const float* head_logits;  // [B, Hq, max_len]
+  float* stat_m;             // [B, Hq] workspace
+  float* stat_l;             // [B, Hq] workspace
+  const int32_t* seq_lens;   // [B]
+  float* scores;             // [B, Hkv, max_len]
+  int32_t batch, q_heads, kv_heads, max_len;
+};
+hipError_t launch_softmax_scores(const SoftmaxScoreArgs& a, hipStream_t stream);
 
 struct SelectArgs {
   const float* scores;      // [B, Hkv, Nmax]
@@ -96,7 +111,8 @@ enum KernelKind : int {
   KERNEL_COMBINE = 3,
   KERNEL_SELECT = 4,
   KERNEL_APPEND = 5,
-  KERNEL_KINDS = 6
+  KERNEL_SOFTMAX_SCORES = 6,
+  KERNEL_KINDS = 7
 };
 // Records a begin event on `stream` when timing is on; returns a token (-1: untimed) and the end event.
 int timing_begin(hipStream_t stream, hipEvent_t* end);

@@ -15,6 +15,7 @@ namespace ppsa {
 static_assert(KERNEL_ATTN_FULL == PPSA_KERNEL_ATTN_FULL && KERNEL_ATTN_FULL_SCORES == PPSA_KERNEL_ATTN_FULL_SCORES &&
                   KERNEL_ATTN_SPARSE == PPSA_KERNEL_ATTN_SPARSE && KERNEL_COMBINE == PPSA_KERNEL_COMBINE &&
                   KERNEL_SELECT == PPSA_KERNEL_SELECT && KERNEL_APPEND == PPSA_KERNEL_APPEND &&
+                  KERNEL_SOFTMAX_SCORES == PPSA_KERNEL_SOFTMAX_SCORES &&
                   KERNEL_KINDS == PPSA_KERNEL_KINDS,
               "internal kernel kinds must match ppsa_kernel_kind");
 
@@ -167,6 +168,7 @@ const char* ppsa_timing_kernel_name(int32_t kind) {
     case KERNEL_COMBINE: return "merge of split partials";
     case KERNEL_SELECT: return "top-k selection";
     case KERNEL_APPEND: return "append of a token's K/V rows";
+    case KERNEL_SOFTMAX_SCORES: return "softmax-weight selection scores";
     default: return "unknown";
   }
 }

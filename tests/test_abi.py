@@ -143,7 +143,7 @@ def test_timing_api_without_gpu_work():
     assert res["dropped"] == 0
     assert all(res[k] == (0, 0.0) for k in ppsa.KERNEL_KEYS)
     nk = ppsa.PPSA_KERNEL_KINDS
-    assert nk == len(ppsa.KERNEL_KEYS) == 6
+    assert nk == len(ppsa.KERNEL_KEYS) == 7
     counts = (ctypes.c_int32 * nk)()
     ms = (ctypes.c_double * nk)()
     assert LIB.ppsa_timing_read(counts, ms, nk - 1, None) == ppsa.PPSA_ERR_INVALID_ARG
@@ -176,12 +176,13 @@ def test_append_kv_validation():
 
 def test_select_mode_validation():
     d = dims()
-    for mode in (-1, 2, 7):
-        assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, mode, FAKE, None, 0, None) == \
-            ppsa.PPSA_ERR_INVALID_ARG
-        codes = ppsa.schedule_codes("FFX")
+    codes = ppsa.schedule_codes("FFX")
+    for mode in (-1, 3, 7):
         assert LIB.ppsa_decode_step_ex(ctypes.byref(d), 3, codes, FAKE, FAKE, FAKE, FAKE, 16, mode, FAKE, FAKE, None,
                                        FAKE, 1 << 30, None) == ppsa.PPSA_ERR_INVALID_ARG
+    for mode in (-1, ppsa.PPSA_SELECT_SOFTMAX, 7):  # softmax weights need head logits: decode steps only
+        assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, mode, FAKE, None, 0, None) == \
+            ppsa.PPSA_ERR_INVALID_ARG
     # A valid mode reaches the usual checks (idx misaligned for int32 here, so nothing is launched).
     assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, ppsa.PPSA_SELECT_SHARED,
                                    ctypes.c_void_p(0x100002), None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG

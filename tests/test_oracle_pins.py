@@ -333,6 +333,34 @@ def pin_shared_equals_per_head_with_one_kv_head():
     np.testing.assert_array_equal(a, b)
 
 
+def pin_softmax_selection_brute_force():
+    """Softmax-weight selection: each head's weights written out with math.exp, summed over the group."""
+    B, Hkv, g, d, n_max, k, scale = 1, 2, 3, 4, 8, 3, 0.7
+    q = RNG.standard_normal((B, Hkv * g, d)).astype(np.float32) * 2
+    K = RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32)
+    V = RNG.standard_normal((B, Hkv, n_max, d)).astype(np.float32)
+    _, sel, sc = O.decode_layer("X", q, K, V, [7], g, k, scale, "f32", None, "softmax")
+    for h in range(Hkv):
+        tot = [0.0] * 7
+        for hq in range(h * g, (h + 1) * g):
+            a = [sum(float(q[0, hq, i]) * float(K[0, h, n, i]) for i in range(d)) * scale for n in range(7)]
+            z = sum(math.exp(x - max(a)) for x in a)
+            for n in range(7):
+                tot[n] += math.exp(a[n] - max(a)) / z
+        want = [np.float32(x) for x in tot]
+        np.testing.assert_allclose(sc[0, h, :7], want, rtol=1e-6)
+        assert as_set(sel[0, h]) == rank_select(want, k)
+
+
+def pin_softmax_selection_group_one_orders_like_logits():
+    q = RNG.standard_normal((2, 3, 6)).astype(np.float32)
+    K = RNG.standard_normal((2, 3, 20, 6)).astype(np.float32)
+    V = RNG.standard_normal((2, 3, 20, 6)).astype(np.float32)
+    _, a, _ = O.decode_layer("X", q, K, V, [20, 13], 1, 6, 0.4, "f32", None, "kv_head")
+    _, b, _ = O.decode_layer("X", q, K, V, [20, 13], 1, 6, 0.4, "f32", None, "softmax")
+    np.testing.assert_array_equal(a, b)
+
+
 PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets, pin_select_vs_torch_sort,
         pin_q_zero_selects_prefix, pin_full_vs_torch_sdpa, pin_q_zero_mean, pin_single_row,
         pin_two_rows_closed_form, pin_dominant_key, pin_softmax_rows_sum_to_one, pin_group_score_is_sum_of_heads,
@@ -340,7 +368,8 @@ PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets
         pin_sparse_skips_invalid_and_counts_repeats, pin_reuse_most_recent_selection, pin_empty_and_short,
         pin_multistep_full_vs_torch_sdpa_on_concatenated_cache, pin_multistep_new_dominant_key_is_selected,
         pin_append_into_full_cache_changes_nothing, pin_shared_selection_brute_force,
-        pin_shared_equals_per_head_with_one_kv_head]
+        pin_shared_equals_per_head_with_one_kv_head, pin_softmax_selection_brute_force,
+        pin_softmax_selection_group_one_orders_like_logits]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -414,6 +443,11 @@ def _mut_shared_first_head(q_all, K_all, n_live, group, scale):
     return O.logits(q_all[:group], K_all[0, :n_live], scale).sum(axis=0).astype(np.float32)
 
 
+def _mut_softmax_unnormalised(q, K, n_live, scale):
+    a = O.logits(q, K[:n_live], scale)
+    return np.exp(a - a.max(axis=1, keepdims=True)).sum(axis=0).astype(np.float32)
+
+
 MUTANTS = {
     "drop_scale": ("logits", _mut_no_scale),
     "ties_to_higher_index": ("select_topk", _mut_ties_high),
@@ -424,6 +458,7 @@ MUTANTS = {
     "append_over_last_row": ("append_kv", _mut_append_over_last_row),
     "append_without_growth": ("append_kv", _mut_append_without_growth),
     "shared_score_of_first_head_only": ("shared_selection_scores", _mut_shared_first_head),
+    "softmax_weights_not_normalised": ("softmax_selection_scores", _mut_softmax_unnormalised),
 }
 
 

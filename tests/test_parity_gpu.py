@@ -354,3 +354,46 @@ def test_select_topk_shared_exact(n):
             want = oracle.select_topk(tot[b, :m], k)
             for h in range(H):
                 assert np.array_equal(got[b, h], np.sort(want[want >= 0]).tolist() + [-1] * (k - min(k, m))), (n, k, b, h)
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "llama3-8b-gqa-32k", "llama3-70b-ragged-10k"])
+def test_decode_step_softmax_selection(name):
+    """Softmax-weight selection (a group ranks a position by the sum of its heads' softmax weights). The
+    written scores are within 1e-4 relative of the oracle's (logits carry ~1e-6 relative float32 error,
+    exp2 and the normaliser about as much, so 1e-4 leaves a tenfold margin); the set passes the band
+    rule with a band of 1e-4 of s_k and is exactly the top-k of its own scores; outputs are checked
+    layer by layer, sparse layers against the GPU's own set. Covers the vector-ALU path (fp32, group 1),
+    split and single-split matrix-core launches (groups 4 and 8)."""
+    wl = REDUCED[name]
+    gen = synth.Generator(wl)
+    say(f"[parity] softmax selection {name}: lens={gen.seq_lens.tolist()}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    n_sel = wl.schedule().count("X")
+    scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32, device=DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores, select_mode="softmax")
+    torch.cuda.synchronize()
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    scale = oracle.default_scale(wl.head_dim)
+    g = wl.group
+    sel = -1
+    for layer, kind in enumerate(wl.schedule()):
+        qh, kh, vh = host[layer]
+        if kind == "X":
+            sel += 1
+            check_layer("F", wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None, None,
+                        f"softmax {name} layer {layer} (X output)")
+            for b in range(wl.batch):
+                n = min(max(int(gen.seq_lens[b]), 0), wl.max_len)
+                for h in range(wl.kv_heads):
+                    ref = oracle.softmax_selection_scores(oracle.widen(qh[b, h * g:(h + 1) * g], wl.dtype),
+                                                          oracle.widen(kh[b, h], wl.dtype), n, scale).astype(np.float64)
+                    got = sc_h[sel, b, h, :n].astype(np.float64)
+                    assert np.all(np.abs(got - ref) <= 1e-4 * np.abs(ref) + 1e-12), (layer, b, h)
+                    ok, msg, _ = compare.check_selection_band(idx_h[sel, b, h], ref, n, wl.topk, band=0.0, rel_band=1e-4)
+                    assert ok, f"softmax {name} layer {layer} b={b} h={h}: {msg}"
+                    assert compare.check_selection_exact(idx_h[sel, b, h], sc_h[sel, b, h], n, wl.topk), (layer, b, h)
+        else:
+            check_layer(kind, wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None,
+                        idx_h[sel] if sel >= 0 else None, f"softmax {name} layer {layer} ({kind})")
+    say(f"[parity] softmax selection {name}: ok")
