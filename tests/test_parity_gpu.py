@@ -237,13 +237,26 @@ def test_select_topk_paths(n, kind):
                 assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, m):] == -1)
 
 
-def test_full_size_bench_workload_sampled():
-    """The benchmark workload at full size, launch configuration as timed; sampled units checked."""
-    wl = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+FULL_SIZE_UNITS = {
+    "llama3-8b-gqa-32k": [(0, 0), (1, 3), (2, 5), (3, 7)],
+    "llama2-7b-10k": [(0, 0), (0, 17), (0, 31)],
+    "llama2-7b-100k": [(0, 0), (0, 21)],
+    "llama3-70b-ragged-10k": [(0, 0), (3, 4), (7, 7)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE_UNITS))
+def test_full_size_workload_sampled(name):
+    """Every multi-layer workload at its full size, in the launch configuration the benchmark times;
+    sampled (batch row, KV head) units checked layer by layer against the oracle."""
+    wl = synth.WORKLOADS[name]
     gen = synth.Generator(wl)
-    units = [(0, 0), (1, 3), (2, 5), (3, 7)]
-    say(f"[parity] full-size {wl.name}: generating {wl.layers} layers")
-    q, k, v, lens, host = torch_io.upload(wl, gen, DEV, keep_units=units)
+    units = FULL_SIZE_UNITS[name]
+    say(f"[parity] full-size {wl.name}: generating {wl.layers} layers, B={wl.batch} Hkv={wl.kv_heads} "
+        f"N={wl.max_len} k={wl.topk}, units {units}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV, keep_units=units,
+                                          progress=lambda layer: say(f"[parity]   layer {layer} resident")
+                                          if layer % 8 == 7 else None)
     n_sel = wl.schedule().count("X")
     scores = torch.empty((n_sel, wl.batch, wl.kv_heads, wl.max_len), dtype=torch.float32, device=DEV)
     ws = ppsa.alloc_workspace(ppsa.make_dims(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.max_len,
