@@ -315,6 +315,29 @@ def main():
         comparison["softmax_selection"] = {"schedule": "".join(sched), "select_mode": "softmax",
                                            "step_us": round(us, 1), "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
                                            "overlap_with_default_set": overlap(idx_default, idx)}
+
+        # Coverage budget instead of a fixed k (capped at k): prune the lowest-mass tail past tau.
+        tau = 0.8
+
+        def coverage_step():
+            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
+                             select_mode="coverage", coverage_tau=tau)
+
+        coverage_step()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
+            coverage_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        kept = (idx >= 0).sum(dim=-1).float()
+        comparison["coverage_selection"] = {"schedule": "".join(sched), "select_mode": "coverage", "tau": tau,
+                                            "cap": wl.topk, "step_us": round(us, 1),
+                                            "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
+                                            "kept_per_unit": {"mean": round(float(kept.mean()), 1),
+                                                              "min": int(kept.min()), "max": int(kept.max())}}
     if comparison:
         log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
 

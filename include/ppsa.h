@@ -131,11 +131,20 @@ int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* 
  * and normaliser L of the same full-attention pass); `scores`, when given,
  * receives these sums. The workspace from ppsa_workspace_bytes(dims, topk)
  * with topk > 0 covers the head logits this needs.
+ * PPSA_SELECT_COVERAGE (decode steps only): the softmax-weight sums again,
+ * but the number kept per (batch row, KV head) is a coverage budget instead
+ * of topk: with masses m_n = sum / group (about 1 in total), the positions
+ * are pruned from the lowest mass upward (equal masses from the higher
+ * position) until the pruned mass exceeds coverage_tau; the rest are kept,
+ * at most topk of them (the token-sparse page's dynamic token coverage
+ * paragraph). Masses are summed in 24-bit fixed point, so the budget does
+ * not depend on summation order (masses below 2^-25 count as zero).
  */
 typedef enum ppsa_select_mode {
   PPSA_SELECT_PER_KV_HEAD = 0,
   PPSA_SELECT_SHARED = 1,
-  PPSA_SELECT_SOFTMAX = 2
+  PPSA_SELECT_SOFTMAX = 2,
+  PPSA_SELECT_COVERAGE = 3
 } ppsa_select_mode;
 
 /* ppsa_select_topk with a selection mode (PPSA_SELECT_PER_KV_HEAD or PPSA_SELECT_SHARED; any other
@@ -171,12 +180,14 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
-/* ppsa_decode_step with a selection mode for its PPSA_FULL_SELECT layers (scores are written per KV
- * head either way; an unknown mode returns PPSA_ERR_INVALID_ARG). */
+/* ppsa_decode_step with a selection mode for its PPSA_FULL_SELECT layers and, for
+ * PPSA_SELECT_COVERAGE, the threshold coverage_tau in [0, 1) (ignored otherwise). scores, when given,
+ * receives the quantity ranked per KV head (logit sums, or softmax-weight sums in the softmax and
+ * coverage modes). An unknown mode or a tau outside [0, 1) returns PPSA_ERR_INVALID_ARG. */
 int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                         const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
-                        int32_t select_mode, void* out, int32_t* idx, float* scores, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        int32_t select_mode, float coverage_tau, void* out, int32_t* idx, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Append one decode token to the caches (section 2, problem definition:
@@ -228,7 +239,8 @@ typedef enum ppsa_kernel_kind {
   PPSA_KERNEL_SELECT = 4,           /* top-k selection */
   PPSA_KERNEL_APPEND = 5,           /* append of a token's K/V rows */
   PPSA_KERNEL_SOFTMAX_SCORES = 6,   /* softmax-weight selection scores */
-  PPSA_KERNEL_KINDS = 7
+  PPSA_KERNEL_COVERAGE = 7,         /* coverage budget per unit */
+  PPSA_KERNEL_KINDS = 8
 } ppsa_kernel_kind;
 
 int ppsa_timing_enable(int32_t capacity);

@@ -48,6 +48,12 @@ Readings where the page is silent (each repeated in the design notes):
            KV head), ranked by the float32 rounding of the sum over the
            group's query heads of the softmax weight each head gives the
            position in this layer's full attention.
+  R-cover  (selection variant, off by default; the token-sparse page's
+           dynamic token coverage) with masses m_n = softmax-weight sum / group
+           (about 1 in total), positions are pruned in ascending mass order,
+           equal masses from the higher position, until the pruned mass
+           exceeds tau times the total; the rest are kept (at most k), ranked
+           like any selection.
   R-append a decode step first stores the new token's K and V rows at
            position N_b of every layer and KV head, and N_b becomes N_b + 1;
            the step's attention then sees them. A full cache (N_b = Nmax)
@@ -145,8 +151,21 @@ def softmax_selection_scores(q, K, n_live: int, scale: float) -> np.ndarray:
     return softmax_weights(logits(q, K[:n_live], scale)).sum(axis=0).astype(np.float32)
 
 
+def coverage_budget(scores: np.ndarray, group: int, tau: float) -> int:
+    """Positions kept by the coverage rule (R-cover): n minus the smallest count p of lowest-mass
+    positions whose mass sum exceeds tau * total; 0 when no count does."""
+    m = np.asarray(scores, dtype=np.float32).astype(np.float64) / group
+    n = m.shape[0]
+    if n == 0:
+        return 0
+    order = np.lexsort((-np.arange(n), m))  # mass ascending, then position descending
+    csum = np.cumsum(m[order])
+    over = np.nonzero(csum > tau * csum[-1])[0]
+    return 0 if over.size == 0 else int(n - (over[0] + 1))
+
+
 def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: float, dtype: str,
-                 selection=None, select_mode: str = "kv_head"):
+                 selection=None, select_mode: str = "kv_head", coverage_tau: float = 0.0):
     """One layer of the decode step [S2, S3F].
 
     q [B, Hq, d], K and V [B, Hkv, Nmax, d] in storage form; `selection`
@@ -180,12 +199,16 @@ def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: flo
                 Vb = widen(V[b, h, :n], dtype)
                 out[b, heads] = attend(qg, Kb, Vb, scale)
                 if kind == FULL_SELECT:
-                    if select_mode == "softmax":
+                    if select_mode in ("softmax", "coverage"):
                         s = softmax_selection_scores(qg, Kb, n, scale)
                     else:
                         s = selection_scores(qg, Kb, n, scale)
                     scores[b, h, :n] = s
-                    new_sel[b, h] = select_topk(s, topk)
+                    if select_mode == "coverage":
+                        kk = min(coverage_budget(s, group, coverage_tau), topk)
+                        new_sel[b, h, :kk] = select_topk(s, kk)[:kk]
+                    else:
+                        new_sel[b, h] = select_topk(s, topk)
         if kind == FULL_SELECT and select_mode == "shared":
             s = shared_selection_scores(widen(q[b], dtype), widen(K[b, :, :n], dtype), n, group, scale)
             new_sel[b, :] = select_topk(s, topk)
@@ -193,7 +216,7 @@ def decode_layer(kind: str, q, K, V, seq_lens, group: int, topk: int, scale: flo
 
 
 def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, scale: float, dtype: str,
-                select_mode: str = "kv_head"):
+                select_mode: str = "kv_head", coverage_tau: float = 0.0):
     """Whole decode step: run `schedule` (list of F/X/S) over per-layer inputs.
 
     q_layers[l] is [B, Hq, d]; kv_layers(l) returns (K, V) for layer l.
@@ -204,7 +227,7 @@ def decode_step(schedule, q_layers, kv_layers, seq_lens, group: int, topk: int, 
     for layer, kind in enumerate(schedule):
         K, V = kv_layers(layer)
         out, selection, _ = decode_layer(kind, q_layers[layer], K, V, seq_lens, group, topk, scale, dtype,
-                                         selection, select_mode)
+                                         selection, select_mode, coverage_tau)
         outs.append(out)
         if kind == FULL_SELECT:
             sels.append(selection)

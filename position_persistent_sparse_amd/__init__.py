@@ -25,11 +25,12 @@ PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
-PPSA_SELECT_PER_KV_HEAD, PPSA_SELECT_SHARED, PPSA_SELECT_SOFTMAX = 0, 1, 2
-SELECT_MODES = {"kv_head": PPSA_SELECT_PER_KV_HEAD, "shared": PPSA_SELECT_SHARED, "softmax": PPSA_SELECT_SOFTMAX}
-PPSA_KERNEL_KINDS = 7
+PPSA_SELECT_PER_KV_HEAD, PPSA_SELECT_SHARED, PPSA_SELECT_SOFTMAX, PPSA_SELECT_COVERAGE = 0, 1, 2, 3
+SELECT_MODES = {"kv_head": PPSA_SELECT_PER_KV_HEAD, "shared": PPSA_SELECT_SHARED, "softmax": PPSA_SELECT_SOFTMAX,
+                "coverage": PPSA_SELECT_COVERAGE}
+PPSA_KERNEL_KINDS = 8
 KERNEL_KEYS = ("attn_full", "attn_full_scores", "attn_sparse", "combine", "select", "append",
-               "softmax_scores")  # ppsa_kernel_kind order
+               "softmax_scores", "coverage")  # ppsa_kernel_kind order
 
 
 class Dims(ctypes.Structure):
@@ -59,7 +60,8 @@ def _load():
     lib.ppsa_full_attn_select.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_select_topk.argtypes = [dp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_select_topk_ex.argtypes = [dp, vp, vp, i32, i32, vp, vp, sz, vp]
-    lib.ppsa_decode_step_ex.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.ppsa_decode_step_ex.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp, vp, sz,
+                                        vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
@@ -197,7 +199,8 @@ def schedule_codes(schedule) -> ctypes.Array:
 
 
 def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, idx=None, scores=None,
-                workspace=None, scale: float = 0.0, sched_codes=None, select_mode: str = "kv_head"):
+                workspace=None, scale: float = 0.0, sched_codes=None, select_mode: str = "kv_head",
+                coverage_tau: float = 0.0):
     """One decode step; returns (out [L,B,Hq,d], idx [S,B,Hkv,topk]) with S = selection layers."""
     _check_tensors(q, k_cache, v_cache, seq_lens, layered=True)
     dims = _dims_of(q, k_cache, scale, layered=True)
@@ -210,7 +213,8 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
     ws = alloc_workspace(dims, topk if n_sel else 0, q.device) if workspace is None else workspace
     codes = schedule_codes(schedule) if sched_codes is None else sched_codes
     _check(_lib.ppsa_decode_step_ex(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                    _ptr(seq_lens), int(topk), SELECT_MODES[select_mode], _ptr(out), _ptr(idx),
+                                    _ptr(seq_lens), int(topk), SELECT_MODES[select_mode], float(coverage_tau),
+                                    _ptr(out), _ptr(idx),
                                     _ptr(scores), _ptr(ws), ws.numel(), _stream(q.device)), "ppsa_decode_step_ex")
     return out, idx
 

@@ -52,6 +52,7 @@ struct Plan {
   int max_splits = 0;
   size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
   size_t off_heads = 0, off_fm = 0, off_fl = 0;  // softmax-weight selection: head logits, final max / sum
+  size_t off_unitk = 0;                           // coverage budget per unit
   bool full_ok = true;    // false: full layers would need more splits than one unit may have
   bool sparse_ok = true;  // false: the budget needs more splits than one unit may have
   bool mfma = false;
@@ -110,6 +111,7 @@ Plan make_plan(const ppsa_dims& d, int topk) {
     p.off_heads = off; off = align_up(off + heads * d.max_seq_len * sizeof(float));
     p.off_fm = off; off = align_up(off + heads * sizeof(float));
     p.off_fl = off; off = align_up(off + heads * sizeof(float));
+    p.off_unitk = off; off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * sizeof(int32_t));
   }
   p.total = off;
   return p;
@@ -172,8 +174,10 @@ int run_combine(const Ctx& c, int splits, void* out) {
   return finish(timed(KERNEL_COMBINE, c.stream, [&] { return launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream); }));
 }
 
-int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx, int mode) {
+int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx, int mode,
+               const int32_t* unit_k = nullptr) {
   SelectArgs s{};
+  s.unit_k = unit_k;
   s.shared = mode == PPSA_SELECT_SHARED ? 1 : 0;
   s.scores = scores;
   s.seq_lens = seq_lens;
@@ -186,12 +190,13 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
 }
 
 int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
-             int topk, float* scores, int32_t* idx, int select_mode) {
+             int topk, float* scores, int32_t* idx, int select_mode, float tau = 0.0f) {
   AttnArgs a = base_args(c, q, k, v, seq_lens, out);
   a.splits = c.plan.full_splits;
   a.rows_per_split = c.plan.full_rows;
   const bool select = idx != nullptr;
-  const bool softmax = select && select_mode == PPSA_SELECT_SOFTMAX;
+  const bool coverage = select && select_mode == PPSA_SELECT_COVERAGE;
+  const bool softmax = select && (select_mode == PPSA_SELECT_SOFTMAX || coverage);
   if (select) a.scores = scores ? scores : reinterpret_cast<float*>(c.ws + c.plan.off_scores);
   if (softmax) a.head_logits = reinterpret_cast<float*>(c.ws + c.plan.off_heads);
   const int mode = softmax ? MODE_FULL_HEADS : (select ? MODE_FULL_SCORES : MODE_FULL);
@@ -215,7 +220,21 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
     rc = finish(timed(KERNEL_SOFTMAX_SCORES, c.stream, [&] { return launch_softmax_scores(sa, c.stream); }));
     if (rc != PPSA_OK) return rc;
   }
-  return run_select(c, a.scores, seq_lens, topk, idx, softmax ? PPSA_SELECT_PER_KV_HEAD : select_mode);
+  int32_t* unit_k = nullptr;
+  if (coverage) {
+    CoverageArgs ca{};
+    ca.scores = a.scores;
+    ca.seq_lens = seq_lens;
+    ca.unit_k = unit_k = reinterpret_cast<int32_t*>(c.ws + c.plan.off_unitk);
+    ca.batch = c.d->batch;
+    ca.kv_heads = c.d->num_kv_heads;
+    ca.max_len = c.d->max_seq_len;
+    ca.group = c.d->num_q_heads / c.d->num_kv_heads;
+    ca.tau = tau;
+    rc = finish(timed(KERNEL_COVERAGE, c.stream, [&] { return launch_coverage(ca, c.stream); }));
+    if (rc != PPSA_OK) return rc;
+  }
+  return run_select(c, a.scores, seq_lens, topk, idx, softmax ? PPSA_SELECT_PER_KV_HEAD : select_mode, unit_k);
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
@@ -370,15 +389,16 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
   return ppsa_decode_step_ex(dims, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, PPSA_SELECT_PER_KV_HEAD,
-                             out, idx, scores, workspace, workspace_bytes, stream);
+                             0.0f, out, idx, scores, workspace, workspace_bytes, stream);
 }
 
 int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                         const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
-                        int32_t select_mode, void* out, int32_t* idx, float* scores, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  if (select_mode != PPSA_SELECT_PER_KV_HEAD && select_mode != PPSA_SELECT_SHARED && select_mode != PPSA_SELECT_SOFTMAX)
-    return PPSA_ERR_INVALID_ARG;
+                        int32_t select_mode, float coverage_tau, void* out, int32_t* idx, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (select_mode < PPSA_SELECT_PER_KV_HEAD || select_mode > PPSA_SELECT_COVERAGE) return PPSA_ERR_INVALID_ARG;
+  if (select_mode == PPSA_SELECT_COVERAGE && !(coverage_tau >= 0.0f && coverage_tau < 1.0f))
+    return PPSA_ERR_INVALID_ARG;  // also rejects NaN
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if (num_layers < 0 || (num_layers > 0 && !schedule)) return PPSA_ERR_INVALID_ARG;
@@ -423,7 +443,7 @@ int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t
       case PPSA_FULL_SELECT:
         ++sel;
         rc = run_full(c, ql, kl, vl, seq_lens, ol, topk, scores ? scores + sel * score_slot : nullptr,
-                      idx + sel * idx_slot, select_mode);
+                      idx + sel * idx_slot, select_mode, coverage_tau);
         break;
       default:
         rc = run_sparse(c, ql, kl, vl, seq_lens, idx + sel * idx_slot, topk, ol);

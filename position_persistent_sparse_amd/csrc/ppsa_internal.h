@@ -68,7 +68,21 @@ struct SelectArgs {
   int32_t* idx;             // [B, Hkv, topk]
   int32_t batch, kv_heads, max_len, topk;
   int32_t shared;           // 1: one set per batch row over the sum of its KV heads' scores
+  const int32_t* unit_k;    // optional [units]: per-unit budget (capped by topk)
 };
+
+// Coverage budget (coverage.hip): per (b, kv) unit, with masses m_n = scores[unit, n] / group (the
+// group's softmax-weight sums, total ~1), the number of positions kept once the lowest-mass tail is
+// pruned until its mass exceeds tau: unit_k = n_live - p, p the smallest count of lowest-mass
+// positions (ascending mass, equal masses from the higher position) whose mass sum exceeds tau.
+struct CoverageArgs {
+  const float* scores;      // [B, Hkv, max_len]
+  const int32_t* seq_lens;  // [B]
+  int32_t* unit_k;          // [B * Hkv]
+  int32_t batch, kv_heads, max_len, group;
+  float tau;
+};
+hipError_t launch_coverage(const CoverageArgs& a, hipStream_t stream);
 
 // Vector-ALU attention pass (any supported dtype / head_dim / group).
 // Rows one workgroup covers per loop trip, and the largest sparse split
@@ -112,7 +126,8 @@ enum KernelKind : int {
   KERNEL_SELECT = 4,
   KERNEL_APPEND = 5,
   KERNEL_SOFTMAX_SCORES = 6,
-  KERNEL_KINDS = 7
+  KERNEL_COVERAGE = 7,
+  KERNEL_KINDS = 8
 };
 // Records a begin event on `stream` when timing is on; returns a token (-1: untimed) and the end event.
 int timing_begin(hipStream_t stream, hipEvent_t* end);

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int b = SHARED ? unit : unit / a.kv_heads;
   const int n = min(max(a.seq_lens[b], 0), a.max_len);
-  const int k_eff = min(a.topk, n);
+  int k_eff = min(a.topk, n);
+  if (a.unit_k) k_eff = min(k_eff, max(a.unit_k[unit], 0));  // per-unit budget (coverage variant)
   // Score rows summed per position (all KV heads of the batch row when SHARED) and idx rows written.
   const int rows = SHARED ? a.kv_heads : 1;
   const float* s = a.scores + (size_t)unit * rows * a.max_len;
@@ -101,10 +102,11 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
     for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = pos;
   };
 
-  if (k_eff == n) {  // every live position is kept (includes n == 0)
-    for (int i = tid; i < a.topk; i += kThreads) emit(i, i < n ? i : -1);
+  if (k_eff == n || k_eff == 0) {  // every live position is kept, or none (includes n == 0)
+    for (int i = tid; i < a.topk; i += kThreads) emit(i, i < k_eff ? i : -1);
     return;
   }
+  for (int i = k_eff + tid; i < a.topk; i += kThreads) emit(i, -1);  // slots past a per-unit budget
 
   // Rows start 16-byte aligned when the base is and hold a multiple of 4 scores.
   const bool aligned = (a.max_len % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) % 16) == 0;

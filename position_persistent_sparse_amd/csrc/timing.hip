@@ -15,7 +15,7 @@ namespace ppsa {
 static_assert(KERNEL_ATTN_FULL == PPSA_KERNEL_ATTN_FULL && KERNEL_ATTN_FULL_SCORES == PPSA_KERNEL_ATTN_FULL_SCORES &&
                   KERNEL_ATTN_SPARSE == PPSA_KERNEL_ATTN_SPARSE && KERNEL_COMBINE == PPSA_KERNEL_COMBINE &&
                   KERNEL_SELECT == PPSA_KERNEL_SELECT && KERNEL_APPEND == PPSA_KERNEL_APPEND &&
-                  KERNEL_SOFTMAX_SCORES == PPSA_KERNEL_SOFTMAX_SCORES &&
+                  KERNEL_SOFTMAX_SCORES == PPSA_KERNEL_SOFTMAX_SCORES && KERNEL_COVERAGE == PPSA_KERNEL_COVERAGE &&
                   KERNEL_KINDS == PPSA_KERNEL_KINDS,
               "internal kernel kinds must match ppsa_kernel_kind");
 
@@ -136,7 +136,7 @@ int ppsa_timing_enable(int32_t capacity) {
     // Timing only: no system-scope fence (cache writeback and invalidate) when the event is recorded,
     // which would otherwise sit between the timed kernels and lengthen every bracket.
     if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
-      destroy_pool(s);
+      (void)destroy_pool(s);
       return PPSA_ERR_HIP;
     }
     s.created.push_back(e);
@@ -169,6 +169,7 @@ const char* ppsa_timing_kernel_name(int32_t kind) {
     case KERNEL_SELECT: return "top-k selection";
     case KERNEL_APPEND: return "append of a token's K/V rows";
     case KERNEL_SOFTMAX_SCORES: return "softmax-weight selection scores";
+    case KERNEL_COVERAGE: return "coverage budget per unit";
     default: return "unknown";
   }
 }

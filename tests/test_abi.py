@@ -143,7 +143,7 @@ def test_timing_api_without_gpu_work():
     assert res["dropped"] == 0
     assert all(res[k] == (0, 0.0) for k in ppsa.KERNEL_KEYS)
     nk = ppsa.PPSA_KERNEL_KINDS
-    assert nk == len(ppsa.KERNEL_KEYS) == 7
+    assert nk == len(ppsa.KERNEL_KEYS) == 8
     counts = (ctypes.c_int32 * nk)()
     ms = (ctypes.c_double * nk)()
     assert LIB.ppsa_timing_read(counts, ms, nk - 1, None) == ppsa.PPSA_ERR_INVALID_ARG
@@ -177,10 +177,11 @@ def test_append_kv_validation():
 def test_select_mode_validation():
     d = dims()
     codes = ppsa.schedule_codes("FFX")
-    for mode in (-1, 3, 7):
-        assert LIB.ppsa_decode_step_ex(ctypes.byref(d), 3, codes, FAKE, FAKE, FAKE, FAKE, 16, mode, FAKE, FAKE, None,
-                                       FAKE, 1 << 30, None) == ppsa.PPSA_ERR_INVALID_ARG
-    for mode in (-1, ppsa.PPSA_SELECT_SOFTMAX, 7):  # softmax weights need head logits: decode steps only
+    for mode, tau in ((-1, 0.0), (4, 0.0), (7, 0.0), (ppsa.PPSA_SELECT_COVERAGE, -0.1),
+                      (ppsa.PPSA_SELECT_COVERAGE, 1.0), (ppsa.PPSA_SELECT_COVERAGE, float("nan"))):
+        assert LIB.ppsa_decode_step_ex(ctypes.byref(d), 3, codes, FAKE, FAKE, FAKE, FAKE, 16, mode, tau, FAKE, FAKE,
+                                       None, FAKE, 1 << 30, None) == ppsa.PPSA_ERR_INVALID_ARG, (mode, tau)
+    for mode in (-1, ppsa.PPSA_SELECT_SOFTMAX, ppsa.PPSA_SELECT_COVERAGE, 7):  # need head logits: steps only
         assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, mode, FAKE, None, 0, None) == \
             ppsa.PPSA_ERR_INVALID_ARG
     # A valid mode reaches the usual checks (idx misaligned for int32 here, so nothing is launched).

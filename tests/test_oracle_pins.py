@@ -361,6 +361,38 @@ def pin_softmax_selection_group_one_orders_like_logits():
     np.testing.assert_array_equal(a, b)
 
 
+def pin_coverage_uniform_closed_form():
+    """q = 0 gives every position the same mass 1/n; pruning until the pruned mass exceeds tau takes
+    floor(tau n) + 1 positions, from the highest position down."""
+    n, g = 8, 2
+    q = np.zeros((1, g, 4), np.float32)
+    K = RNG.standard_normal((1, 1, n, 4)).astype(np.float32)
+    V = RNG.standard_normal((1, 1, n, 4)).astype(np.float32)
+    for tau, kept in ((0.25, 5), (0.0, 7), (0.5, 3), (0.9, 0)):
+        _, sel, _ = O.decode_layer("X", q, K, V, [n], g, n, 1.0, "f32", None, "coverage", tau)
+        assert as_set(sel[0, 0]) == list(range(kept)), (tau, as_set(sel[0, 0]))
+
+
+def pin_coverage_brute_force():
+    """Random masses: sort ascending (equal masses from the higher position), prune while the pruned
+    mass has not yet exceeded tau of the total, keep the rest -- written out as a loop."""
+    g, n = 3, 11
+    q = RNG.standard_normal((1, g, 5)).astype(np.float32)
+    K = RNG.standard_normal((1, 1, n, 5)).astype(np.float32)
+    V = RNG.standard_normal((1, 1, n, 5)).astype(np.float32)
+    for tau in (0.05, 0.3, 0.7):
+        _, sel, sc = O.decode_layer("X", q, K, V, [n], g, n, 0.8, "f32", None, "coverage", tau)
+        m = [float(x) / g for x in sc[0, 0, :n]]
+        order = sorted(range(n), key=lambda i: (m[i], -i))
+        total, pruned, acc = sum(m), [], 0.0
+        for i in order:
+            if acc > tau * total:
+                break
+            acc += m[i]
+            pruned.append(i)
+        assert as_set(sel[0, 0]) == sorted(set(range(n)) - set(pruned)), tau
+
+
 PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets, pin_select_vs_torch_sort,
         pin_q_zero_selects_prefix, pin_full_vs_torch_sdpa, pin_q_zero_mean, pin_single_row,
         pin_two_rows_closed_form, pin_dominant_key, pin_softmax_rows_sum_to_one, pin_group_score_is_sum_of_heads,
@@ -369,7 +401,8 @@ PINS = [pin_bf16_bits, pin_select_rank_definition, pin_select_exhaustive_subsets
         pin_multistep_full_vs_torch_sdpa_on_concatenated_cache, pin_multistep_new_dominant_key_is_selected,
         pin_append_into_full_cache_changes_nothing, pin_shared_selection_brute_force,
         pin_shared_equals_per_head_with_one_kv_head, pin_softmax_selection_brute_force,
-        pin_softmax_selection_group_one_orders_like_logits]
+        pin_softmax_selection_group_one_orders_like_logits, pin_coverage_uniform_closed_form,
+        pin_coverage_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -413,8 +446,10 @@ def _mut_no_renorm(q, K, V, scale):
 _orig_decode_layer = O.decode_layer
 
 
-def _mut_first_selection(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection=None, select_mode="kv_head"):
-    out, sel, sc = _orig_decode_layer(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection, select_mode)
+def _mut_first_selection(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection=None, select_mode="kv_head",
+                         coverage_tau=0.0):
+    out, sel, sc = _orig_decode_layer(kind, q, K, V, seq_lens, group, topk, scale, dtype, selection, select_mode,
+                                      coverage_tau)
     if kind == "X" and selection is not None:
         sel = selection  # keeps reusing the first set
     return out, sel, sc
@@ -448,6 +483,16 @@ def _mut_softmax_unnormalised(q, K, n_live, scale):
     return np.exp(a - a.max(axis=1, keepdims=True)).sum(axis=0).astype(np.float32)
 
 
+def _mut_coverage_reaching(scores, group, tau):
+    m = np.asarray(scores, dtype=np.float32).astype(np.float64) / group
+    n = m.shape[0]
+    if n == 0:
+        return 0
+    csum = np.cumsum(m[np.lexsort((-np.arange(n), m))])
+    over = np.nonzero(csum >= tau * csum[-1])[0]  # stops on reaching tau instead of exceeding it
+    return 0 if over.size == 0 else int(n - (over[0] + 1))
+
+
 MUTANTS = {
     "drop_scale": ("logits", _mut_no_scale),
     "ties_to_higher_index": ("select_topk", _mut_ties_high),
@@ -459,6 +504,7 @@ MUTANTS = {
     "append_without_growth": ("append_kv", _mut_append_without_growth),
     "shared_score_of_first_head_only": ("shared_selection_scores", _mut_shared_first_head),
     "softmax_weights_not_normalised": ("softmax_selection_scores", _mut_softmax_unnormalised),
+    "coverage_stops_on_reaching_tau": ("coverage_budget", _mut_coverage_reaching),
 }
 
 

@@ -410,3 +410,60 @@ def test_decode_step_softmax_selection(name):
             check_layer(kind, wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None,
                         idx_h[sel] if sel >= 0 else None, f"softmax {name} layer {layer} ({kind})")
     say(f"[parity] softmax selection {name}: ok")
+
+
+@pytest.mark.parametrize("name,tau,cap", [("tiny-f32", 0.2, None), ("llama3-8b-gqa-32k", 0.1, None),
+                                          ("llama3-70b-ragged-10k", 0.5, None), ("llama3-8b-gqa-32k", 0.1, 64)])
+def test_decode_step_coverage_budget(name, tau, cap):
+    """Coverage budget: per unit, the lowest-mass positions are pruned until their mass exceeds tau; the
+    kept count must sit at a crossing of the oracle's cumulative mass within 2e-4 (masses carry 1e-4
+    relative error from the softmax-weight sums), the set must pass the relative band rule for that
+    count and be exactly the top of the GPU's own scores; outputs are checked layer by layer. With a
+    cap (topk below the budget) the set is the top-cap positions."""
+    base = REDUCED[name]
+    wl = base.with_(topk=cap if cap else base.max_len)
+    gen = synth.Generator(wl)
+    say(f"[parity] coverage {name} tau={tau} topk={wl.topk}: lens={gen.seq_lens.tolist()}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    n_sel = wl.schedule().count("X")
+    scores = torch.full((n_sel, wl.batch, wl.kv_heads, wl.max_len), float("nan"), dtype=torch.float32, device=DEV)
+    out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk, scores=scores, select_mode="coverage",
+                                coverage_tau=tau)
+    torch.cuda.synchronize()
+    out_h = widen_out(torch_io.from_torch(out), wl)
+    idx_h, sc_h = idx.cpu().numpy(), scores.cpu().numpy()
+    scale = oracle.default_scale(wl.head_dim)
+    g = wl.group
+    sel = -1
+    kept = []
+    for layer, kind in enumerate(wl.schedule()):
+        qh, kh, vh = host[layer]
+        if kind != "X":
+            check_layer(kind, wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None,
+                        idx_h[sel] if sel >= 0 else None, f"coverage {name} layer {layer} ({kind})")
+            continue
+        sel += 1
+        check_layer("F", wl, qh, kh, vh, gen.seq_lens, out_h[layer], None, None, None,
+                    f"coverage {name} layer {layer} (X output)")
+        for b in range(wl.batch):
+            n = min(max(int(gen.seq_lens[b]), 0), wl.max_len)
+            for h in range(wl.kv_heads):
+                ref = oracle.softmax_selection_scores(oracle.widen(qh[b, h * g:(h + 1) * g], wl.dtype),
+                                                      oracle.widen(kh[b, h], wl.dtype), n, scale)
+                row = idx_h[sel, b, h]
+                k_gpu = int(np.sum(row >= 0))
+                assert np.all(row[k_gpu:] == -1)
+                if cap is None:
+                    m = ref.astype(np.float64) / g
+                    csum = np.concatenate([[0.0], np.cumsum(m[np.lexsort((-np.arange(n), m))])])
+                    p = n - k_gpu  # pruned count
+                    thr = tau * csum[-1]
+                    assert p >= 1 and csum[p - 1] <= thr + 2e-4 and csum[p] > thr - 2e-4, (layer, b, h, p)
+                    assert abs(k_gpu - oracle.coverage_budget(ref, g, tau)) <= max(3, n // 100), (layer, b, h)
+                else:
+                    assert k_gpu == min(cap, oracle.coverage_budget(ref, g, tau)), (layer, b, h)
+                kept.append(k_gpu)
+                ok, msg, _ = compare.check_selection_band(row, ref, n, k_gpu, band=0.0, rel_band=1e-4)
+                assert ok, f"coverage {name} layer {layer} b={b} h={h}: {msg}"
+                assert compare.check_selection_exact(row, sc_h[sel, b, h], n, k_gpu), (layer, b, h)
+    say(f"[parity] coverage {name} tau={tau}: ok, kept per unit {min(kept)}..{max(kept)}")

@@ -67,7 +67,7 @@ def test_launch_timing_counts_and_results(inputs):
     assert res["combine"][0] == len(sched)  # every layer of this shape is cut into several splits
     assert res["dropped"] == 0
     for key in ppsa.KERNEL_KEYS:
-        if key in ("append", "softmax_scores"):  # not part of a default decode step
+        if key in ("append", "softmax_scores", "coverage"):  # not part of a default decode step
             assert res[key] == (0, 0.0)
         else:
             assert res[key][1] > 0.0, key
