@@ -240,9 +240,12 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
     gtm &= sp.live;
     eqm &= sp.live;
     const uint32_t n_gt = __popc(gtm), n_eq = __popc(eqm);
-    uint32_t tot_gt, tot_eq;
-    const uint32_t gt_before = gt_seen + block_exclusive_scan<kThreads>(n_gt, scan_lds, &tot_gt);
-    const uint32_t eq_before = eq_seen + block_exclusive_scan<kThreads>(n_eq, scan_lds, &tot_eq);
+    // One scan of both counts: per super-round each total is at most 32768, so the counts of keys
+    // == T (low 16 bits) never carry into those of keys > T (high 16 bits).
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan<kThreads>((n_gt << 16) | n_eq, scan_lds, &tot);
+    const uint32_t gt_before = gt_seen + (before >> 16), eq_before = eq_seen + (before & 0xFFFFu);
+    const uint32_t tot_gt = tot >> 16, tot_eq = tot & 0xFFFFu;
     // Saturating forms only: hipcc 7.2 turned a guarded `needed - before` feeding min() into an
     // unconditional one assumed not to wrap, which dropped the clamp on the slot below.
     const uint32_t room = max(needed_eq, eq_before) - eq_before;  // keys == T this thread may take
