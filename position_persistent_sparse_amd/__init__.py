@@ -128,6 +128,18 @@ def _require(cond, msg):
         raise ValueError(msg)
 
 
+def _check_buffer(t, shape, dtype, device, name):
+    """A caller-provided output or state buffer: the library writes it by shape, so it must match."""
+    _require(tuple(t.shape) == tuple(int(x) for x in shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.is_contiguous() and t.device == device, f"{name} must be contiguous on {device}")
+
+
+def _workspace_nbytes(ws, device):
+    _require(ws.is_contiguous() and ws.device == device, "workspace must be contiguous on the tensors' device")
+    return ws.numel() * ws.element_size()
+
+
 def _check_tensors(q, k_cache, v_cache, seq_lens, layered=False):
     nd = 4 if layered else 3
     _require(q.dim() == nd and k_cache.dim() == nd + 1, "q must be [(L,) B, Hq, d] and K [(L,) B, Hkv, N, d]")
@@ -140,15 +152,18 @@ def _check_tensors(q, k_cache, v_cache, seq_lens, layered=False):
     for t in (q, k_cache, v_cache, seq_lens):
         _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous GPU tensors")
     _require(seq_lens.dtype == torch.int32 and seq_lens.shape == (q.shape[-3],), "seq_lens must be int32 [B]")
+    _require(q.device == k_cache.device == v_cache.device == seq_lens.device, "tensors must share one device")
 
 
 def full_attn(q, k_cache, v_cache, seq_lens, out=None, workspace=None, scale: float = 0.0):
     _check_tensors(q, k_cache, v_cache, seq_lens)
     dims = _dims_of(q, k_cache, scale)
     out = torch.empty_like(q) if out is None else out
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
     ws = alloc_workspace(dims, 0, q.device) if workspace is None else workspace
     _check(_lib.ppsa_full_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                               _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)), "ppsa_full_attn")
+                               _ptr(out), _ptr(ws), _workspace_nbytes(ws, q.device), _stream(q.device)),
+           "ppsa_full_attn")
     return out
 
 
@@ -157,12 +172,16 @@ def full_attn_select(q, k_cache, v_cache, seq_lens, topk: int, out=None, scores=
     _check_tensors(q, k_cache, v_cache, seq_lens)
     dims = _dims_of(q, k_cache, scale)
     out = torch.empty_like(q) if out is None else out
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
     if idx is None:
         idx = torch.empty((dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
+    _check_buffer(idx, (dims.batch, dims.num_kv_heads, int(topk)), torch.int32, q.device, "idx")
+    if scores is not None:
+        _check_buffer(scores, (dims.batch, dims.num_kv_heads, dims.max_seq_len), torch.float32, q.device, "scores")
     ws = alloc_workspace(dims, topk, q.device) if workspace is None else workspace
     _check(_lib.ppsa_full_attn_select(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                                      int(topk), _ptr(out), _ptr(scores), _ptr(idx), _ptr(ws), ws.numel(),
-                                      _stream(q.device)), "ppsa_full_attn_select")
+                                      int(topk), _ptr(out), _ptr(scores), _ptr(idx), _ptr(ws),
+                                      _workspace_nbytes(ws, q.device), _stream(q.device)), "ppsa_full_attn_select")
     return out, idx
 
 
@@ -171,9 +190,11 @@ def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: s
     _require(scores.dim() == 3 and scores.dtype == torch.float32 and scores.is_contiguous() and scores.is_cuda,
              "scores must be contiguous float32 [B, Hkv, N] on the GPU")
     B, Hkv, N = scores.shape
+    _check_buffer(seq_lens, (B,), torch.int32, scores.device, "seq_lens")
     dims = make_dims(B, num_q_heads or Hkv, Hkv, 128, N, PPSA_F32)
     if idx is None:
         idx = torch.empty((B, Hkv, int(topk)), dtype=torch.int32, device=scores.device)
+    _check_buffer(idx, (B, Hkv, int(topk)), torch.int32, scores.device, "idx")
     _check(_lib.ppsa_select_topk_ex(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), int(topk), SELECT_MODES[mode],
                                     _ptr(idx), None, 0, _stream(scores.device)), "ppsa_select_topk_ex")
     return idx
@@ -184,12 +205,14 @@ def sparse_attn(q, k_cache, v_cache, seq_lens, idx, out=None, workspace=None, sc
     dims = _dims_of(q, k_cache, scale)
     _require(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 3
              and tuple(idx.shape[:2]) == (dims.batch, dims.num_kv_heads), "idx must be int32 [B, Hkv, topk]")
+    _require(idx.device == q.device, "idx must be on the tensors' device")
     topk = idx.shape[2]
     out = torch.empty_like(q) if out is None else out
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
     ws = alloc_workspace(dims, topk, q.device) if workspace is None else workspace
     _check(_lib.ppsa_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                                 _ptr(idx), int(topk), _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)),
-           "ppsa_sparse_attn")
+                                 _ptr(idx), int(topk), _ptr(out), _ptr(ws), _workspace_nbytes(ws, q.device),
+                                 _stream(q.device)), "ppsa_sparse_attn")
     return out
 
 
@@ -208,14 +231,21 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
     _require(len(schedule) == L, "schedule length must equal the layer count")
     n_sel = sum(1 for k in schedule if k in ("X", PPSA_FULL_SELECT))
     out = torch.empty_like(q) if out is None else out
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
     if idx is None and n_sel:
         idx = torch.empty((n_sel, dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
+    if n_sel:
+        _check_buffer(idx, (n_sel, dims.batch, dims.num_kv_heads, int(topk)), torch.int32, q.device, "idx")
+    if scores is not None:
+        _check_buffer(scores, (n_sel, dims.batch, dims.num_kv_heads, dims.max_seq_len), torch.float32, q.device,
+                      "scores")
     ws = alloc_workspace(dims, topk if n_sel else 0, q.device) if workspace is None else workspace
     codes = schedule_codes(schedule) if sched_codes is None else sched_codes
     _check(_lib.ppsa_decode_step_ex(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(seq_lens), int(topk), SELECT_MODES[select_mode], float(coverage_tau),
                                     _ptr(out), _ptr(idx),
-                                    _ptr(scores), _ptr(ws), ws.numel(), _stream(q.device)), "ppsa_decode_step_ex")
+                                    _ptr(scores), _ptr(ws), _workspace_nbytes(ws, q.device), _stream(q.device)),
+           "ppsa_decode_step_ex")
     return out, idx
 
 

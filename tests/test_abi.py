@@ -187,3 +187,17 @@ def test_select_mode_validation():
     # A valid mode reaches the usual checks (idx misaligned for int32 here, so nothing is launched).
     assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, ppsa.PPSA_SELECT_SHARED,
                                    ctypes.c_void_p(0x100002), None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_mismatched_buffers():
+    """Caller-provided buffers are written by shape on the device, so the binding checks them first."""
+    import torch
+
+    dev = torch.device("cpu")
+    good = torch.empty((2, 3, 4), dtype=torch.int32)
+    ppsa._check_buffer(good, (2, 3, 4), torch.int32, dev, "idx")
+    for bad in (torch.empty((2, 3, 5), dtype=torch.int32), torch.empty((2, 3, 4), dtype=torch.int64),
+                torch.empty((2, 4, 3), dtype=torch.int32).transpose(1, 2)):
+        with pytest.raises(ValueError):
+            ppsa._check_buffer(bad, (2, 3, 4), torch.int32, dev, "idx")
+    assert ppsa._workspace_nbytes(torch.empty(10, dtype=torch.float32), dev) == 40
