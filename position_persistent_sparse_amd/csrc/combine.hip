@@ -9,11 +9,13 @@
 // (M = -inf) outputs zeros.
 //
 // The pass moves about 0.5-1 % of a layer's bytes, so it is latency bound:
-// one 256-thread workgroup per (b, query head); every thread issues all of
-// its partial-output loads before waiting (threads t and t+128 take the
-// even / odd splits of dim t%128), while wave 0 loads the (m, l) pairs and
-// turns them into weights in LDS. Summation order is fixed, so results are
-// bitwise reproducible.
+// one wave per (b, query head), no LDS and no barrier. Every lane issues
+// the partial-output loads of its dims for the first 16 splits before the
+// max is known; the lanes then hold one split's (m, l) each, the max and
+// the normaliser are wave reductions, and each split's weight reaches the
+// lanes by a shuffle. Summation order is fixed, so results are bitwise
+// reproducible. (A 256-thread workgroup per row with the weights in LDS
+// took about 0.8 us longer per launch.)
 #include <math.h>
 
 #include "device_common.h"
@@ -22,9 +24,6 @@
 
 namespace ppsa {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kBatch = 32;  // partial loads in flight per thread and trip
 
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = bf16_round(v); }
@@ -42,79 +41,53 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  static_assert(kThreads % D == 0, "threads per dim must be whole");
-  constexpr int kLanesPerDim = kThreads / D;  // 2 for D = 128, 4 for D = 64
-  __shared__ float sm_w[kMaxSplitsPerUnit];
-  __shared__ float sm_part[kThreads];
-  __shared__ float sm_norm;
-
-  const int row = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
+  constexpr int kDims = D / kWave;  // dims per lane: 1 (D = 64) or 2 (D = 128)
+  constexpr int kB = 16;            // splits whose partial outputs are loaded per batch
+  const int row = blockIdx.x, lane = threadIdx.x;
   const int S = a.splits;
-  const int d = tid % D, sub = tid / D;
   const float* pm = a.part_m + (size_t)row * S;
   const float* pl = a.part_l + (size_t)row * S;
-  const float* po = a.part_o + (size_t)row * S * D + d;
-
-  if (tid < kWave) {
-    float mv[kMaxSplitsPerUnit / kWave], lv[kMaxSplitsPerUnit / kWave];
+  const float* po = a.part_o + (size_t)row * S * D + lane;
+  // First batch of partial outputs in flight before the max is known.
+  float v[kB][kDims];
 #pragma unroll
-    for (int i = 0; i < kMaxSplitsPerUnit / kWave; ++i) {
-      const int s = tid + i * kWave;
-      mv[i] = s < S ? pm[s] : -INFINITY;
-      lv[i] = s < S ? pl[s] : 0.0f;
+  for (int j = 0; j < kB; ++j)
+#pragma unroll
+    for (int e = 0; e < kDims; ++e) v[j][e] = j < S ? po[(size_t)j * D + kWave * e] : 0.0f;
+  float mx = -INFINITY;
+  for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, pm[s]);
+  mx = wave_max(mx);
+  const float ms = mx == -INFINITY ? 0.0f : mx;
+  float lsum = 0.0f, acc[kDims];
+#pragma unroll
+  for (int e = 0; e < kDims; ++e) acc[e] = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kWave) {
+    const int s = s0 + lane;
+    float w = 0.0f;
+    if (s < S) {
+      w = __builtin_amdgcn_exp2f(pm[s] - ms);  // -inf (empty split) gives 0
+      lsum += pl[s] * w;
     }
-    float mx = -INFINITY;
+    for (int b0 = s0; b0 < min(S, s0 + kWave); b0 += kB) {
+      if (b0 != 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxSplitsPerUnit / kWave; ++i) mx = fmaxf(mx, mv[i]);
-    mx = wave_max(mx);
-    const float ms = mx == -INFINITY ? 0.0f : mx;
-    float ls = 0.0f;
+        for (int j = 0; j < kB; ++j)
 #pragma unroll
-    for (int i = 0; i < kMaxSplitsPerUnit / kWave; ++i) {
-      const int s = tid + i * kWave;
-      const float w = __builtin_amdgcn_exp2f(mv[i] - ms);  // -inf (empty split) gives 0
-      if (s < S) sm_w[s] = w;
-      ls += lv[i] * w;
-    }
-    ls = wave_sum(ls);
-    if (tid == 0) sm_norm = ls;
-  }
-
-  // Splits sub, sub + kLanesPerDim, ... of dim d: the first batch of loads is
-  // issued before the barrier that publishes the weights.
-  constexpr int kStride = kBatch * kLanesPerDim;
-  float v[kBatch];
+          for (int e = 0; e < kDims; ++e) v[j][e] = b0 + j < S ? po[(size_t)(b0 + j) * D + kWave * e] : 0.0f;
+      }
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) {
-    const int s = sub + j * kLanesPerDim;
-    v[j] = s < S ? po[(size_t)s * D] : 0.0f;
-  }
-  __syncthreads();
-  float acc = 0.0f;
-  for (int s0 = sub;;) {
+      for (int j = 0; j < kB; ++j) {
+        const float wj = __shfl(w, b0 - s0 + j);
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = s0 + j * kLanesPerDim;
-      if (s < S) acc += v[j] * sm_w[s];
-    }
-    s0 += kStride;
-    if (s0 >= S) break;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int s = s0 + j * kLanesPerDim;
-      v[j] = s < S ? po[(size_t)s * D] : 0.0f;
+        for (int e = 0; e < kDims; ++e) acc[e] += v[j][e] * wj;
+      }
     }
   }
-  sm_part[tid] = acc;
-  __syncthreads();
-  if (sub == 0) {
-    float tot = acc;
+  lsum = wave_sum(lsum);
 #pragma unroll
-    for (int j = 1; j < kLanesPerDim; ++j) tot += sm_part[tid + j * D];
-    const float L = sm_norm;
-    store_out(reinterpret_cast<T*>(a.out) + (size_t)row * D + d, L > 0.0f ? tot / L : 0.0f);
-  }
+  for (int e = 0; e < kDims; ++e)
+    store_out(reinterpret_cast<T*>(a.out) + (size_t)row * D + lane + kWave * e, lsum > 0.0f ? acc[e] / lsum : 0.0f);
 }
 
 }  // namespace
@@ -122,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   if (a.splits < 1 || a.splits > kMaxSplitsPerUnit) return hipErrorInvalidValue;
-  const dim3 grid(a.rows), block(kThreads);
+  const dim3 grid(a.rows), block(kWave);
   if (dtype == PPSA_BF16) {
     if (head_dim == 128) combine_kernel<uint16_t, 128><<<grid, block, 0, stream>>>(a);
     else if (head_dim == 64) combine_kernel<uint16_t, 64><<<grid, block, 0, stream>>>(a);
