@@ -41,6 +41,15 @@ struct Layout {
   static constexpr int ROWS_TRIP = ROWS_WAVE * kWaves;
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a K or V row; rows are read once per layer, so the load carries the nontemporal hint.
+template <typename P>
+__device__ __forceinline__ uint4 load_row16(const P* p) {
+  const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 __device__ __forceinline__ void widen16(const uint4& w, float (&x)[8]) {
   x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
   x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
@@ -128,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(AttnArgs a) {
         row = valid[u] ? slot : slot_end - 1;
       }
       pos[u] = row;
-      kr[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)row * D);
-      vr[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)row * D);
+      kr[u] = load_row16(kbase + (size_t)row * D);
+      vr[u] = load_row16(vbase + (size_t)row * D);
     }
 
     float x[kUnroll][G];  // logits in log2 units, -inf for invalid rows
