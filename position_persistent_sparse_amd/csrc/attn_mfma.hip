@@ -58,6 +58,16 @@ constexpr int kMaxSparseRowsMfma = 2048;
 // layer); a split's LDS (wave outputs + scores) stays within 64 KiB.
 constexpr size_t kMaxLdsBytes = 65536;
 constexpr float kLazyLog2 = 8.0f;
+// Sparse launches of kWaves waves load K rows whole (four 256-byte rows per load instruction, the
+// V pattern) and move them into the matrix-core operand layout through a wave-private LDS tile of
+// kTile rows, padded to 272 bytes per row so that the sixteen rows one read instruction touches fall
+// on distinct banks. A gathered row read as sixteen quarter rows per instruction (the direct
+// operand layout) measured 1.1 us slower per 64 MiB layer in a load-only probe.
+constexpr int kKRowPitch = kD * 2 + 16;
+constexpr int kKTileBytes = kTile * kKRowPitch;  // 8704 bytes: also holds the wave's output (<= 16 heads)
+
+template <int MODE, int WAVES>
+constexpr bool k_via_lds() { return MODE == MODE_SPARSE && WAVES == kWaves; }
 
 struct Tile {
   uint4 k[2][4];    // [block][c]: K[row 16*blk + n][32c + 8g .. +8]
@@ -86,10 +96,26 @@ __device__ __forceinline__ uint4 load16(const char* base, uint32_t off) {
   }
 }
 
-template <int MODE, bool STREAM>
+template <int MODE, bool STREAM, bool KT>
 __device__ __forceinline__ void load_tile(Tile& t, const char* kb, const char* vb, int tslot, int slot0,
                                           int slot_end, const int32_t* rows, int g, int n) {
   t.valid = 0u;
+  if constexpr (KT) {
+    // K and V rows alike: lane (g, n) loads bytes 16n .. 16n+15 of rows 16 blk + 4g + i.
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = tslot + 16 * blk + 4 * g + i;
+        const int p = slot < slot_end ? rows[slot - slot0] : -1;
+        const bool ok = p >= 0;
+        const uint32_t off = (uint32_t)(ok ? p : 0) * (kD * 2) + 16u * n;
+        t.valid |= (uint32_t)ok << (4 * blk + i);
+        t.k[blk][i] = load16<STREAM>(kb, off);
+        t.v[blk][i] = load16<STREAM>(vb, off);
+      }
+    return;
+  }
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     {
@@ -128,17 +154,39 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
   return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
 }
 
+// Whole-row K pieces (lane (g, n): rows 16 blk + 4g + i, bytes 16n ..) to the operand layout
+// (lane (g, n): row 16 blk + n, bytes 16g + 64c ..) through the wave's own LDS tile. LDS
+// instructions of one wave execute in order, so the reads see the writes, and the next tile's
+// writes come after these reads.
+__device__ __forceinline__ void k_to_operand(Tile& t, char* ktile, int g, int n) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(ktile + (16 * blk + 4 * g + i) * kKRowPitch + 16 * n) = t.k[blk][i];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      t.k[blk][c] = *reinterpret_cast<const uint4*>(ktile + (16 * blk + n) * kKRowPitch + 16 * g + 64 * c);
+}
+
 template <int MODE, int WAVES, bool STREAM>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int kThreads = WAVES * kWave;
   constexpr bool kScores = MODE == MODE_FULL_SCORES || MODE == MODE_FULL_HEADS;
-  extern __shared__ float dyn[];  // [WAVES][group][kD] wave outputs, then staged sparse positions
+  constexpr bool KT = k_via_lds<MODE, WAVES>();
+  // [WAVES] x (wave stride) wave outputs -- with KT each wave's region is its K tile, reused for the
+  // output once the tile loop is done -- then the staged sparse positions or scores.
+  extern __shared__ float dyn[];
   __shared__ float sm_m[WAVES][kMaxGroup];
   __shared__ float sm_l[WAVES][kMaxGroup];
   const int group = a.group;
+  const int wstride = KT ? kKTileBytes / 4 : group * kD;  // floats per wave region
   float* sm_o = dyn;
-  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * group * kD);  // sparse mode
-  float* sm_sc = dyn + WAVES * group * kD;                                    // full+scores mode
+  int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * wstride);  // sparse mode
+  float* sm_sc = dyn + WAVES * wstride;                                        // full+scores mode
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -262,7 +310,8 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   // tiles per wave at two waves per SIMD, and a software-pipelined loop, measured slower.
   for (int ti = wave; ti < ntiles; ti += WAVES) {
     Tile t;
-    load_tile<MODE, STREAM>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
+    load_tile<MODE, STREAM, KT>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
+    if constexpr (KT) k_to_operand(t, reinterpret_cast<char*>(sm_o + wave * wstride), g, n);
     process(t, ti);
   }
 
@@ -277,7 +326,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * g + j;
     if (h < group) {
-      float* dst = sm_o + (wave * group + h) * kD + 8 * n;
+      float* dst = sm_o + wave * wstride + h * kD + 8 * n;
 #pragma unroll
       for (int t = 0; t < 8; ++t) dst[t] = acc[t][j];
     }
@@ -299,7 +348,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
       const float c = exp2_fast(sm_m[w][h] - ms);
-      o += sm_o[(w * group + h) * kD + d] * c;
+      o += sm_o[w * wstride + h * kD + d] * c;
       lsum += sm_l[w][h] * c;
     }
     if (single) {
@@ -345,7 +394,8 @@ hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t str
 
 // Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions or scores.
 size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
-  size_t lds = (size_t)waves * a.group * kD * sizeof(float);
+  const bool kt = mode == MODE_SPARSE && waves == kWaves;  // k_via_lds
+  size_t lds = (size_t)waves * (kt ? (size_t)kKTileBytes : a.group * kD * sizeof(float));
   if (mode == MODE_SPARSE || mode == MODE_FULL_SCORES || mode == MODE_FULL_HEADS) lds += (size_t)a.rows_per_split * 4;
   return lds;
 }
