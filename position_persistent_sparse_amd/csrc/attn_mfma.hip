@@ -58,16 +58,21 @@ constexpr int kMaxSparseRowsMfma = 2048;
 // layer); a split's LDS (wave outputs + scores) stays within 64 KiB.
 constexpr size_t kMaxLdsBytes = 65536;
 constexpr float kLazyLog2 = 8.0f;
-// Sparse launches of kWaves waves load K rows whole (four 256-byte rows per load instruction, the
-// V pattern) and move them into the matrix-core operand layout through a wave-private LDS tile of
-// kTile rows, padded to 272 bytes per row so that the sixteen rows one read instruction touches fall
-// on distinct banks. A gathered row read as sixteen quarter rows per instruction (the direct
-// operand layout) measured 1.1 us slower per 64 MiB layer in a load-only probe.
+// Sparse launches load K rows whole (four 256-byte rows per load instruction, the V pattern) and
+// move them into the matrix-core operand layout through a wave-private LDS buffer of one 16-row
+// block, padded to 272 bytes per row so that the sixteen rows one read instruction touches fall on
+// distinct banks. A gathered row read as sixteen quarter rows per instruction (the direct operand
+// layout) measured 1.1 us slower per 64 MiB layer in a load-only probe.
 constexpr int kKRowPitch = kD * 2 + 16;
-constexpr int kKTileBytes = kTile * kKRowPitch;  // 8704 bytes: also holds the wave's output (<= 16 heads)
+constexpr int kKBlockBytes = 16 * kKRowPitch;  // 4352 bytes per wave
 
-template <int MODE, int WAVES>
-constexpr bool k_via_lds() { return MODE == MODE_SPARSE && WAVES == kWaves; }
+template <int MODE>
+constexpr bool k_via_lds() { return MODE == MODE_SPARSE; }
+
+// Floats of LDS per wave: its output (group heads x kD), or its K block when that is larger.
+__host__ __device__ constexpr int wave_region_floats(bool kt, int group) {
+  return kt && kKBlockBytes / 4 > group * kD ? kKBlockBytes / 4 : group * kD;
+}
 
 struct Tile {
   uint4 k[2][4];    // [block][c]: K[row 16*blk + n][32c + 8g .. +8]
@@ -155,35 +160,35 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
 }
 
 // Whole-row K pieces (lane (g, n): rows 16 blk + 4g + i, bytes 16n ..) to the operand layout
-// (lane (g, n): row 16 blk + n, bytes 16g + 64c ..) through the wave's own LDS tile. LDS
-// instructions of one wave execute in order, so the reads see the writes, and the next tile's
-// writes come after these reads.
-__device__ __forceinline__ void k_to_operand(Tile& t, char* ktile, int g, int n) {
+// (lane (g, n): row 16 blk + n, bytes 16g + 64c ..) through the wave's own 16-row LDS buffer, one
+// block after the other. LDS instructions of one wave execute in order, so each read sees the
+// writes before it and each write comes after the reads of the previous block.
+__device__ __forceinline__ void k_to_operand(Tile& t, char* kbuf, int g, int n) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+  for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(ktile + (16 * blk + 4 * g + i) * kKRowPitch + 16 * n) = t.k[blk][i];
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+      *reinterpret_cast<uint4*>(kbuf + (4 * g + i) * kKRowPitch + 16 * n) = t.k[blk][i];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      t.k[blk][c] = *reinterpret_cast<const uint4*>(ktile + (16 * blk + n) * kKRowPitch + 16 * g + 64 * c);
+      t.k[blk][c] = *reinterpret_cast<const uint4*>(kbuf + n * kKRowPitch + 16 * g + 64 * c);
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 template <int MODE, int WAVES, bool STREAM>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int kThreads = WAVES * kWave;
   constexpr bool kScores = MODE == MODE_FULL_SCORES || MODE == MODE_FULL_HEADS;
-  constexpr bool KT = k_via_lds<MODE, WAVES>();
-  // [WAVES] x (wave stride) wave outputs -- with KT each wave's region is its K tile, reused for the
-  // output once the tile loop is done -- then the staged sparse positions or scores.
+  constexpr bool KT = k_via_lds<MODE>();
+  // [WAVES] x (wave region) wave outputs -- with KT each wave's region is also its K block buffer,
+  // reused for the output once the tile loop is done -- then the staged sparse positions or scores.
   extern __shared__ float dyn[];
   __shared__ float sm_m[WAVES][kMaxGroup];
   __shared__ float sm_l[WAVES][kMaxGroup];
   const int group = a.group;
-  const int wstride = KT ? kKTileBytes / 4 : group * kD;  // floats per wave region
+  const int wstride = wave_region_floats(KT, group);
   float* sm_o = dyn;
   int32_t* sm_rows = reinterpret_cast<int32_t*>(dyn + WAVES * wstride);  // sparse mode
   float* sm_sc = dyn + WAVES * wstride;                                        // full+scores mode
@@ -394,8 +399,7 @@ hipError_t launch_waves(const AttnArgs& a, int mode, size_t lds, hipStream_t str
 
 // Dynamic LDS of a launch: wave partial outputs, then the staged sparse positions or scores.
 size_t lds_bytes(const AttnArgs& a, int mode, int waves) {
-  const bool kt = mode == MODE_SPARSE && waves == kWaves;  // k_via_lds
-  size_t lds = (size_t)waves * (kt ? (size_t)kKTileBytes : a.group * kD * sizeof(float));
+  size_t lds = (size_t)waves * wave_region_floats(mode == MODE_SPARSE, a.group) * sizeof(float);
   if (mode == MODE_SPARSE || mode == MODE_FULL_SCORES || mode == MODE_FULL_HEADS) lds += (size_t)a.rows_per_split * 4;
   return lds;
 }
