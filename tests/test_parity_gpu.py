@@ -125,6 +125,16 @@ def test_other_shapes(dtype, d, g):
     check_step(wl, synth.Generator(wl), f"{dtype} d={d} g={g}")
 
 
+@pytest.mark.parametrize("g", [1, 8, 16])
+def test_multi_split_sparse_groups(g):
+    """Sparse layers cut into several splits per unit (the streaming launch, K rows loaded whole and
+    moved to the matrix-core operand layout through LDS) at group sizes besides the benchmark's 4:
+    ragged lengths, a budget that is not a multiple of the 32-row tile, NaN padding."""
+    wl = synth.Workload("msplit", layers=5, batch=2, q_heads=2 * g, kv_heads=2, head_dim=128, max_len=3000,
+                        topk=1000, dtype="bf16", select_layers=(2, 3), seed=91, min_len=2200)
+    check_step(wl, synth.Generator(wl, pad_mode=synth.PAD_NAN), f"multi-split sparse g={g}")
+
+
 def test_q_zero_ties_select_prefix():
     wl = synth.WORKLOADS["llama3-8b-gqa-32k"].with_(layers=3, batch=1, q_heads=8, kv_heads=2, max_len=1500,
                                                     topk=333, select_layers=(2,))
