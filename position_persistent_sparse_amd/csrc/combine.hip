@@ -12,10 +12,12 @@
 // one wave per (b, query head), no LDS and no barrier. Every lane issues
 // the partial-output loads of its dims for the first 16 splits before the
 // max is known; the lanes then hold one split's (m, l) each, the max and
-// the normaliser are wave reductions, and each split's weight reaches the
-// lanes by a shuffle. Summation order is fixed, so results are bitwise
-// reproducible. (A 256-thread workgroup per row with the weights in LDS
-// took about 0.8 us longer per launch.)
+// the normaliser are wave reductions (DPP within rows of 16 lanes, then the
+// four row results read as scalars), and each split's weight reaches the
+// lanes as a scalar (v_readlane), not through the LDS crossbar. Summation
+// order is fixed, so results are bitwise reproducible. (A 256-thread
+// workgroup per row with the weights in LDS took about 0.8 us longer per
+// launch.)
 #include <math.h>
 
 #include "device_common.h"
@@ -28,16 +30,22 @@ namespace {
 __device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = bf16_round(v); }
 
+// Value of lane L as a wave-uniform scalar.
+__device__ __forceinline__ float lane_value(float x, int L) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), L));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror: every lane of a row holds the row's max
+  return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-  return x;
+  x = group_sum<16>(x);  // every lane of a row holds the row's sum
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
 template <typename T, int D>
@@ -78,7 +86,7 @@ __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < kB; ++j) {
-        const float wj = __shfl(w, b0 - s0 + j);
+        const float wj = lane_value(w, b0 - s0 + j);  // b0 - s0 is a multiple of 16: constant lanes per batch
 #pragma unroll
         for (int e = 0; e < kDims; ++e) acc[e] += v[j][e] * wj;
       }
