@@ -342,20 +342,33 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
     for (int i = tid; i < slot_end - slot0; i += kThreads) dst[i] = sm_sc[i];
   }
 
+  // Per head, once: the largest wave max M, each wave's weight 2^(m_w - M) (written over m_w) and
+  // the merged normaliser, so that each output element is a plain weighted sum over the waves.
+  __shared__ float sm_hm[kMaxGroup], sm_hl[kMaxGroup];
+  if (tid < group) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][tid]);
+    const float ms = mx == -INFINITY ? 0.0f : mx;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float c = exp2_fast(sm_m[w][tid] - ms);
+      sm_m[w][tid] = c;
+      lsum += sm_l[w][tid] * c;
+    }
+    sm_hm[tid] = mx;
+    sm_hl[tid] = lsum;
+  }
+  __syncthreads();
+
   const bool single = a.splits == 1;
   for (int i = tid; i < group * kD; i += kThreads) {
     const int h = i / kD, d = i % kD;
-    float mx = -INFINITY;
+    float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    const float ms = mx == -INFINITY ? 0.0f : mx;
-    float o = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      const float c = exp2_fast(sm_m[w][h] - ms);
-      o += sm_o[w * wstride + h * kD + d] * c;
-      lsum += sm_l[w][h] * c;
-    }
+    for (int w = 0; w < WAVES; ++w) o += sm_o[w * wstride + h * kD + d] * sm_m[w][h];
+    const float lsum = sm_hl[h];
     if (single) {
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)kv * group + h) * kD + d;
       store_elem(op, lsum > 0.0f ? o / lsum : 0.0f);
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
     const size_t row = part_row(a, b, kv, h, split);
     a.part_o[row * kD + d] = o;
     if (d == 0) {
-      a.part_m[row] = mx;
+      a.part_m[row] = sm_hm[h];
       a.part_l[row] = lsum;
     }
   }
