@@ -15,8 +15,9 @@
 //   S^T[row, head] = K[row, :] . q[head, :]
 //       v_mfma_f32_16x16x32_bf16, A = K (lane%16 = row, lane/16 picks 8 of
 //       each 32 dims), B = q (lane%16 = head); four products cover d = 128.
-//       Every lane loads 16-byte pieces of its row; the four lanes of a row
-//       group read 64 contiguous bytes.
+//       Full launches load K straight into that layout (the four lanes of a
+//       row group read 64 contiguous bytes); sparse launches load gathered K
+//       rows whole, like V below, and regroup them through LDS.
 //   The result leaves lane (g = lane/16, n = lane%16) holding the logits of
 //   rows 4g..4g+3 for head n, which is exactly the A operand layout of
 //   v_mfma_f32_16x16x16_bf16 for P[head, row] over those 16 rows, so the
@@ -66,9 +67,6 @@ constexpr float kLazyLog2 = 8.0f;
 constexpr int kKRowPitch = kD * 2 + 16;
 constexpr int kKBlockBytes = 16 * kKRowPitch;  // 4352 bytes per wave
 
-template <int MODE>
-constexpr bool k_via_lds() { return MODE == MODE_SPARSE; }
-
 // Floats of LDS per wave: its output (group heads x kD), or its K block when that is larger.
 __host__ __device__ constexpr int wave_region_floats(bool kt, int group) {
   return kt && kKBlockBytes / 4 > group * kD ? kKBlockBytes / 4 : group * kD;
@@ -101,37 +99,40 @@ __device__ __forceinline__ uint4 load16(const char* base, uint32_t off) {
   }
 }
 
-template <int MODE, bool STREAM, bool KT>
-__device__ __forceinline__ void load_tile(Tile& t, const char* kb, const char* vb, int tslot, int slot0,
-                                          int slot_end, const int32_t* rows, int g, int n) {
+// Sparse launches: K and V rows alike, whole rows per load instruction; lane (g, n) loads bytes
+// 16n .. 16n+15 of rows 16 blk + 4g + i (the slots' positions, staged in LDS; -1 marks a slot
+// with nothing to read, which loads row 0 and stays invalid). k_to_operand then moves K into the
+// operand layout.
+template <bool STREAM>
+__device__ __forceinline__ void load_tile_gathered(Tile& t, const char* kb, const char* vb, int tslot, int slot0,
+                                                   int slot_end, const int32_t* rows, int g, int n) {
   t.valid = 0u;
-  if constexpr (KT) {
-    // K and V rows alike: lane (g, n) loads bytes 16n .. 16n+15 of rows 16 blk + 4g + i.
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+  for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = tslot + 16 * blk + 4 * g + i;
-        const int p = slot < slot_end ? rows[slot - slot0] : -1;
-        const bool ok = p >= 0;
-        const uint32_t off = (uint32_t)(ok ? p : 0) * (kD * 2) + 16u * n;
-        t.valid |= (uint32_t)ok << (4 * blk + i);
-        t.k[blk][i] = load16<STREAM>(kb, off);
-        t.v[blk][i] = load16<STREAM>(vb, off);
-      }
-    return;
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int slot = tslot + 16 * blk + 4 * g + i;
+      const int p = slot < slot_end ? rows[slot - slot0] : -1;
+      const bool ok = p >= 0;
+      const uint32_t off = (uint32_t)(ok ? p : 0) * (kD * 2) + 16u * n;
+      t.valid |= (uint32_t)ok << (4 * blk + i);
+      t.k[blk][i] = load16<STREAM>(kb, off);
+      t.v[blk][i] = load16<STREAM>(vb, off);
+    }
+}
+
+// Full launches: cache rows in order, K straight into the operand layout (lane (g, n): row
+// 16 blk + n, bytes 16g + 64c), V as whole rows (lane (g, n): rows 16 blk + 4g + i, bytes 16n).
+// Slots past the live rows repeat the last live row and stay invalid.
+template <bool STREAM>
+__device__ __forceinline__ void load_tile_rows(Tile& t, const char* kb, const char* vb, int tslot, int slot_end,
+                                               int g, int n) {
+  t.valid = 0u;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     {
       const int slot = tslot + 16 * blk + n;
-      int row;
-      if constexpr (MODE == MODE_SPARSE) {
-        const int p = slot < slot_end ? rows[slot - slot0] : -1;
-        row = p >= 0 ? p : 0;
-      } else {
-        row = slot < slot_end ? slot : slot_end - 1;
-      }
+      const int row = slot < slot_end ? slot : slot_end - 1;
       const uint32_t off = (uint32_t)row * (kD * 2) + 16u * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) t.k[blk][c] = load16<STREAM>(kb, off + 64u * c);
@@ -139,16 +140,8 @@ __device__ __forceinline__ void load_tile(Tile& t, const char* kb, const char* v
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = tslot + 16 * blk + 4 * g + i;
-      int row;
-      bool ok;
-      if constexpr (MODE == MODE_SPARSE) {
-        const int p = slot < slot_end ? rows[slot - slot0] : -1;
-        ok = p >= 0;
-        row = ok ? p : 0;
-      } else {
-        ok = slot < slot_end;
-        row = ok ? slot : slot_end - 1;
-      }
+      const bool ok = slot < slot_end;
+      const int row = ok ? slot : slot_end - 1;
       t.valid |= (uint32_t)ok << (4 * blk + i);
       t.v[blk][i] = load16<STREAM>(vb, (uint32_t)row * (kD * 2) + 16u * n);
     }
@@ -181,7 +174,7 @@ template <int MODE, int WAVES, bool STREAM>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int kThreads = WAVES * kWave;
   constexpr bool kScores = MODE == MODE_FULL_SCORES || MODE == MODE_FULL_HEADS;
-  constexpr bool KT = k_via_lds<MODE>();
+  constexpr bool KT = MODE == MODE_SPARSE;  // K rows through the per-wave LDS buffer
   // [WAVES] x (wave region) wave outputs -- with KT each wave's region is also its K block buffer,
   // reused for the output once the tile loop is done -- then the staged sparse positions or scores.
   extern __shared__ float dyn[];
@@ -315,8 +308,12 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   // tiles per wave at two waves per SIMD, and a software-pipelined loop, measured slower.
   for (int ti = wave; ti < ntiles; ti += WAVES) {
     Tile t;
-    load_tile<MODE, STREAM, KT>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
-    if constexpr (KT) k_to_operand(t, reinterpret_cast<char*>(sm_o + wave * wstride), g, n);
+    if constexpr (KT) {
+      load_tile_gathered<STREAM>(t, kb, vb, slot0 + ti * kTile, slot0, slot_end, sm_rows, g, n);
+      k_to_operand(t, reinterpret_cast<char*>(sm_o + wave * wstride), g, n);
+    } else {
+      load_tile_rows<STREAM>(t, kb, vb, slot0 + ti * kTile, slot_end, g, n);
+    }
     process(t, ti);
   }
 
