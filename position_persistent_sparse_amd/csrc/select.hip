@@ -16,7 +16,8 @@
 //  1. Radix digit 1 (key bits 31..21) over all keys: an LDS histogram and a
 //     workgroup scan of the bins from the top give the bin holding the k-th
 //     largest key and how many keys lie above it.
-//  2. The keys of that bin (the candidates) are copied to LDS; digits 2
+//  2. The keys of that bin (the candidates) are copied to LDS (each thread's
+//     share placed by a workgroup scan of the per-thread counts); digits 2
 //     (bits 20..10) and 3 (bits 9..0) are resolved over the candidates only,
 //     giving the exact key T of the k-th largest score and how many keys
 //     equal to T are still to take (lowest positions first). If the bin does
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
   __shared__ uint32_t scan_lds[kWaves + 1];
   __shared__ uint32_t cand[kMaxCand];
-  __shared__ uint32_t s_digit, s_above, s_ncand;
+  __shared__ uint32_t s_digit, s_above;
 
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int b = SHARED ? unit : unit / a.kv_heads;
@@ -173,7 +174,6 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
 
   // 1. Digit 1 over all keys (padding slots count into the spare bin).
   for (int i = tid; i <= kBins; i += kThreads) hist[i] = 0u;
-  if (tid == 0) s_ncand = 0u;
   __syncthreads();
   for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
 #pragma unroll
@@ -191,12 +191,24 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   __syncthreads();
 
   // 2. Digits 2 and 3, over the candidates (or over all keys if they do not fit).
-  if (use_cand)
+  if (use_cand) {
+    // Each thread marks its candidates in a bit mask; one workgroup scan of the counts gives its
+    // first slot in `cand` (candidates taken in position order, no atomics on a shared counter).
+    uint32_t base = 0u;
     for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
+      uint32_t cm = 0u;
 #pragma unroll
       for (int i = 0; i < kCached; ++i)
-        if (i < sp.per && ((sp.live >> i) & 1u) && (k[i] & mask) == prefix) cand[atomicAdd(&s_ncand, 1u)] = k[i];
+        if (i < sp.per) cm |= (uint32_t)((k[i] & mask) == prefix) << i;
+      cm &= sp.live;
+      uint32_t total;
+      uint32_t slot = base + block_exclusive_scan<kThreads>(__popc(cm), scan_lds, &total);
+#pragma unroll
+      for (int i = 0; i < kCached; ++i)
+        if ((cm >> i) & 1u) cand[slot++] = k[i];
+      base += total;
     });
+  }
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
