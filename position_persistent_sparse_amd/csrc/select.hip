@@ -41,6 +41,10 @@ constexpr int kCached = 32;                    // positions per thread and super
 constexpr int kPerSuper = kCached * kThreads;  // positions per super-round
 constexpr int kBins = 2048;
 constexpr int kMaxCand = 8192;
+// Digit 1 counts into kCopies interleaved histograms (lane % kCopies picks the copy; the copies of a
+// bin sit in adjacent banks), folded afterwards: scores pile into a few hot bins, and lanes of one
+// instruction hitting the same bin serialise.
+constexpr int kCopies = 4;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -86,11 +90,12 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
 template <bool CACHED, bool SHARED>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
+  __shared__ uint32_t histc[(kBins + 1) * kCopies];
   __shared__ uint32_t scan_lds[kWaves + 1];
   __shared__ uint32_t cand[kMaxCand];
   __shared__ uint32_t s_digit, s_above;
 
-  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
   const int b = SHARED ? unit : unit / a.kv_heads;
   const int n = min(max(a.seq_lens[b], 0), a.max_len);
   int k_eff = min(a.topk, n);
@@ -173,13 +178,21 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
   };
 
   // 1. Digit 1 over all keys (padding slots count into the spare bin).
-  for (int i = tid; i <= kBins; i += kThreads) hist[i] = 0u;
+  for (int i = tid; i < (kBins + 1) * kCopies; i += kThreads) histc[i] = 0u;
   __syncthreads();
+  const uint32_t copy = (uint32_t)(lane % kCopies);
   for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
 #pragma unroll
     for (int i = 0; i < kCached; ++i)
-      if (i < sp.per) atomicAdd(&hist[((sp.live >> i) & 1u) ? (k[i] >> 21) : (uint32_t)kBins], 1u);
+      if (i < sp.per) atomicAdd(&histc[(((sp.live >> i) & 1u) ? (k[i] >> 21) : (uint32_t)kBins) * kCopies + copy], 1u);
   });
+  __syncthreads();
+  for (int i = tid; i <= kBins; i += kThreads) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) c += histc[i * kCopies + j];
+    hist[i] = c;
+  }
   __syncthreads();
   uint32_t remaining = (uint32_t)k_eff;
   find_digit<kBins>(hist, remaining, scan_lds, &s_digit, &s_above);
