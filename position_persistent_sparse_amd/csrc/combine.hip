@@ -1,101 +1,20 @@
-// Merge of split attention partials (gfx950).
-//
-// Each split s of a (batch row, query head) leaves m_s (max logit, log2
-// units), l_s = sum 2^(x - m_s) and o_s = sum 2^(x - m_s) V[row]. The
-// softmax over the union of the splits is
-//   out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),   M = max_s m_s,
-// i.e. the attention equation of the TidalDecode review page (section 3,
-// PPSA paragraph) evaluated in pieces. A row with no live position
-// (M = -inf) outputs zeros.
-//
-// The pass moves about 0.5-1 % of a layer's bytes, so it is latency bound:
-// one wave per (b, query head), no LDS and no barrier. Every lane issues
-// the partial-output loads of its dims for the first 16 splits before the
-// max is known; the lanes then hold one split's (m, l) each, the max and
-// the normaliser are wave reductions (DPP within rows of 16 lanes, then the
-// four row results read as scalars), and each split's weight reaches the
-// lanes as a scalar (v_readlane), not through the LDS crossbar. Summation
-// order is fixed, so results are bitwise reproducible. (A 256-thread
-// workgroup per row with the weights in LDS took about 0.8 us longer per
-// launch.)
+// Merge pass of split attention partials (gfx950): one 64-lane wave per
+// (batch row, query head), no LDS and no barrier, running
+// merge::combine_row (combine_row.h). The pass moves about 0.5-1 % of a
+// layer's bytes, so it is latency bound. (A 256-thread workgroup per row
+// with the weights in LDS took about 0.8 us longer per launch.)
 #include <math.h>
 
-#include "device_common.h"
+#include "combine_row.h"
 #include "ppsa.h"
 #include "ppsa_internal.h"
 
 namespace ppsa {
 namespace {
 
-__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = bf16_round(v); }
-
-// Value of lane L as a wave-uniform scalar.
-__device__ __forceinline__ float lane_value(float x, int L) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), L));
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror: every lane of a row holds the row's max
-  return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  x = group_sum<16>(x);  // every lane of a row holds the row's sum
-  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kWave) void combine_kernel(CombineArgs a) {
-  constexpr int kDims = D / kWave;  // dims per lane: 1 (D = 64) or 2 (D = 128)
-  constexpr int kB = 16;            // splits whose partial outputs are loaded per batch
-  const int row = blockIdx.x, lane = threadIdx.x;
-  const int S = a.splits;
-  const float* pm = a.part_m + (size_t)row * S;
-  const float* pl = a.part_l + (size_t)row * S;
-  const float* po = a.part_o + (size_t)row * S * D + lane;
-  // First batch of partial outputs in flight before the max is known.
-  float v[kB][kDims];
-#pragma unroll
-  for (int j = 0; j < kB; ++j)
-#pragma unroll
-    for (int e = 0; e < kDims; ++e) v[j][e] = j < S ? po[(size_t)j * D + kWave * e] : 0.0f;
-  float mx = -INFINITY;
-  for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, pm[s]);
-  mx = wave_max(mx);
-  const float ms = mx == -INFINITY ? 0.0f : mx;
-  float lsum = 0.0f, acc[kDims];
-#pragma unroll
-  for (int e = 0; e < kDims; ++e) acc[e] = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += kWave) {
-    const int s = s0 + lane;
-    float w = 0.0f;
-    if (s < S) {
-      w = __builtin_amdgcn_exp2f(pm[s] - ms);  // -inf (empty split) gives 0
-      lsum += pl[s] * w;
-    }
-    for (int b0 = s0; b0 < min(S, s0 + kWave); b0 += kB) {
-      if (b0 != 0) {
-#pragma unroll
-        for (int j = 0; j < kB; ++j)
-#pragma unroll
-          for (int e = 0; e < kDims; ++e) v[j][e] = b0 + j < S ? po[(size_t)(b0 + j) * D + kWave * e] : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const float wj = lane_value(w, b0 - s0 + j);  // b0 - s0 is a multiple of 16: constant lanes per batch
-#pragma unroll
-        for (int e = 0; e < kDims; ++e) acc[e] += v[j][e] * wj;
-      }
-    }
-  }
-  lsum = wave_sum(lsum);
-#pragma unroll
-  for (int e = 0; e < kDims; ++e)
-    store_out(reinterpret_cast<T*>(a.out) + (size_t)row * D + lane + kWave * e, lsum > 0.0f ? acc[e] / lsum : 0.0f);
+  merge::combine_row<T, D>(a, blockIdx.x, threadIdx.x);
 }
 
 }  // namespace

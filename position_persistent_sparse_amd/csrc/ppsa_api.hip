@@ -161,9 +161,7 @@ hipError_t timed(int kind, hipStream_t stream, F&& launch) {
   return e;
 }
 
-// Merge pass after a multi-split attention launch (a single split writes out itself).
-int run_combine(const Ctx& c, int splits, void* out) {
-  if (splits <= 1) return PPSA_OK;
+CombineArgs combine_args(const Ctx& c, int splits, void* out) {
   CombineArgs cb{};
   cb.part_m = reinterpret_cast<const float*>(c.ws + c.plan.off_m);
   cb.part_l = reinterpret_cast<const float*>(c.ws + c.plan.off_l);
@@ -171,11 +169,19 @@ int run_combine(const Ctx& c, int splits, void* out) {
   cb.out = out;
   cb.rows = c.d->batch * c.d->num_q_heads;
   cb.splits = splits;
+  return cb;
+}
+
+// Merge pass after a multi-split attention launch (a single split writes out itself).
+int run_combine(const Ctx& c, int splits, void* out) {
+  if (splits <= 1) return PPSA_OK;
+  const CombineArgs cb = combine_args(c, splits, out);
   return finish(timed(KERNEL_COMBINE, c.stream, [&] { return launch_combine(cb, c.d->dtype, c.d->head_dim, c.stream); }));
 }
 
+// Top-k selection; with `merge`, the same launch also merges the layer's split partials.
 int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int topk, int32_t* idx, int mode,
-               const int32_t* unit_k = nullptr) {
+               const int32_t* unit_k = nullptr, const CombineArgs* merge = nullptr) {
   SelectArgs s{};
   s.unit_k = unit_k;
   s.shared = mode == PPSA_SELECT_SHARED ? 1 : 0;
@@ -186,7 +192,9 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
   s.kv_heads = c.d->num_kv_heads;
   s.max_len = c.d->max_seq_len;
   s.topk = topk;
-  return finish(timed(KERNEL_SELECT, c.stream, [&] { return launch_select(s, c.stream); }));
+  return finish(timed(KERNEL_SELECT, c.stream, [&] {
+    return merge ? launch_select_merge(s, *merge, c.stream) : launch_select(s, c.stream);
+  }));
 }
 
 int run_full(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens, void* out,
@@ -203,7 +211,11 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
   int rc = finish(timed(select ? KERNEL_ATTN_FULL_SCORES : KERNEL_ATTN_FULL, c.stream, [&] {
     return c.plan.mfma ? launch_attn_mfma(a, mode, c.stream) : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream);
   }));
-  if (rc == PPSA_OK) rc = run_combine(c, a.splits, out);
+  // A selection layer ranked by the logit sums merges its partials (bf16, head_dim 128) inside the
+  // selection launch: the two read disjoint inputs, and the merge then runs beside the top-k work
+  // on CUs it leaves idle instead of as a launch of its own.
+  const bool merge_in_select = select && !softmax && a.splits > 1 && c.d->dtype == PPSA_BF16 && c.d->head_dim == 128;
+  if (rc == PPSA_OK && !merge_in_select) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
   if (softmax) {
     // The scores the selection ranks become the group's softmax-weight sums (written over the logit sums).
@@ -234,7 +246,9 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
     rc = finish(timed(KERNEL_COVERAGE, c.stream, [&] { return launch_coverage(ca, c.stream); }));
     if (rc != PPSA_OK) return rc;
   }
-  return run_select(c, a.scores, seq_lens, topk, idx, softmax ? PPSA_SELECT_PER_KV_HEAD : select_mode, unit_k);
+  const CombineArgs cb = combine_args(c, a.splits, out);
+  return run_select(c, a.scores, seq_lens, topk, idx, softmax ? PPSA_SELECT_PER_KV_HEAD : select_mode, unit_k,
+                    merge_in_select ? &cb : nullptr);
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,

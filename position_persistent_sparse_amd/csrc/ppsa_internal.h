@@ -116,6 +116,8 @@ hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hip
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// One launch for a selection layer's top-k (a) and its merge pass (c; bf16, head_dim 128).
+hipError_t launch_select_merge(const SelectArgs& a, const CombineArgs& c, hipStream_t stream);
 
 // Launch timing (timing.hip). Kinds match the public PPSA_KERNEL_* values.
 enum KernelKind : int {

@@ -29,6 +29,7 @@
 // longer rows reload their super-rounds in each step.
 #include <math.h>
 
+#include "combine_row.h"
 #include "device_common.h"
 #include "ppsa_internal.h"
 
@@ -87,8 +88,19 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
 
 // SHARED: one set per batch row, ranked by the sum of its KV heads' scores and written to every KV
 // head's row of idx (the head-shared selection variant); otherwise one set per (batch row, KV head).
-template <bool CACHED, bool SHARED>
-__global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
+// MERGE: workgroups past the selection units merge the layer's split partials (bf16, head_dim 128),
+// one (batch row, query head) per wave; the merge and the selection read disjoint inputs and write
+// disjoint outputs, so they share the launch and the merge runs on CUs the selection leaves idle.
+template <bool CACHED, bool SHARED, bool MERGE>
+__global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, CombineArgs c) {
+  if constexpr (MERGE) {
+    const int units = SHARED ? a.batch : a.batch * a.kv_heads;
+    if ((int)blockIdx.x >= units) {
+      const int row = ((int)blockIdx.x - units) * kWaves + (int)threadIdx.x / kWave;
+      if (row < c.rows) merge::combine_row<uint16_t, 128>(c, row, (int)threadIdx.x % kWave);
+      return;
+    }
+  }
   __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
   __shared__ uint32_t histc[(kBins + 1) * kCopies];
   __shared__ uint32_t scan_lds[kWaves + 1];
@@ -287,17 +299,34 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a) {
 
 }  // namespace
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  if (a.batch <= 0) return hipSuccess;
-  const dim3 grid(a.shared ? a.batch : a.batch * a.kv_heads), block(kThreads);
+namespace {
+
+template <bool MERGE>
+void launch_select_kernel(const SelectArgs& a, const CombineArgs& c, int extra_blocks, hipStream_t stream) {
+  const dim3 grid((a.shared ? a.batch : a.batch * a.kv_heads) + extra_blocks), block(kThreads);
   const bool cached = a.max_len <= kPerSuper;
   if (a.shared) {
-    if (cached) select_topk_kernel<true, true><<<grid, block, 0, stream>>>(a);
-    else select_topk_kernel<false, true><<<grid, block, 0, stream>>>(a);
+    if (cached) select_topk_kernel<true, true, MERGE><<<grid, block, 0, stream>>>(a, c);
+    else select_topk_kernel<false, true, MERGE><<<grid, block, 0, stream>>>(a, c);
   } else {
-    if (cached) select_topk_kernel<true, false><<<grid, block, 0, stream>>>(a);
-    else select_topk_kernel<false, false><<<grid, block, 0, stream>>>(a);
+    if (cached) select_topk_kernel<true, false, MERGE><<<grid, block, 0, stream>>>(a, c);
+    else select_topk_kernel<false, false, MERGE><<<grid, block, 0, stream>>>(a, c);
   }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
+  if (a.batch <= 0) return hipSuccess;
+  launch_select_kernel<false>(a, CombineArgs{}, 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_merge(const SelectArgs& a, const CombineArgs& c, hipStream_t stream) {
+  if (a.batch <= 0) return hipSuccess;
+  if (c.rows <= 0) return launch_select(a, stream);
+  if (c.splits < 1 || c.splits > kMaxSplitsPerUnit) return hipErrorInvalidValue;
+  launch_select_kernel<true>(a, c, (c.rows + kWaves - 1) / kWaves, stream);
   return hipGetLastError();
 }
 
