@@ -46,6 +46,7 @@ constexpr int kMaxCand = 8192;
 // bin sit in adjacent banks), folded afterwards: scores pile into a few hot bins, and lanes of one
 // instruction hitting the same bin serialise.
 constexpr int kCopies = 4;
+constexpr int kMaskSR = 4;  // super-rounds whose key masks the candidate pass keeps (rows <= 131072)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -136,12 +137,18 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
     int p0, per;
     uint32_t live;
   };
-  auto load_sr = [&](int r, auto& k) -> Span {
+  auto span_of = [&](int r) -> Span {
     const int n_r = min(kPerSuper, n - r * kPerSuper);
     const int per = (n_r + kThreads - 1) / kThreads;
     const int p0 = r * kPerSuper + tid * per;
     const int cnt = max(0, min(per, r * kPerSuper + n_r - p0));
-    const uint32_t live = cnt >= kCached ? 0xFFFFFFFFu : ((1u << cnt) - 1u);
+    return Span{p0, per, cnt >= kCached ? 0xFFFFFFFFu : ((1u << cnt) - 1u)};
+  };
+  auto load_sr = [&](int r, auto& k) -> Span {
+    const Span sp0 = span_of(r);
+    const int p0 = sp0.p0, per = sp0.per;
+    const int cnt = __popc(sp0.live);
+    const uint32_t live = sp0.live;
     if (aligned && (per % 4) == 0 && cnt == per) {
 #pragma unroll
       for (int j = 0; j < kCached / 4; ++j)
@@ -216,23 +223,53 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   __syncthreads();
 
   // 2. Digits 2 and 3, over the candidates (or over all keys if they do not fit).
+  // Rows re-read from memory in every pass (longer than one super-round) but of at most kMaskSR
+  // super-rounds: the candidate pass also keeps, per super-round, the bit masks of this thread's
+  // keys above the threshold bin and in it, and where its candidates went in `cand`; the output
+  // step then needs only those and the candidates, not a third read of the scores.
+  const bool keep_masks = !CACHED && use_cand && n_sr <= kMaskSR;
+  // [super-round][above, cand, first cand slot][thread], in LDS: registers are at their limit here.
+  __shared__ uint32_t sm_marks[CACHED ? 1 : kMaskSR * 3 * kThreads];
+  auto mark = [&](int r, int f) -> uint32_t& { return sm_marks[(r * 3 + f) * kThreads + tid]; };
   if (use_cand) {
     // Each thread marks its candidates in a bit mask; one workgroup scan of the counts gives its
     // first slot in `cand` (candidates taken in position order, no atomics on a shared counter).
     uint32_t base = 0u;
-    for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
-      uint32_t cm = 0u;
+    struct Marks {
+      uint32_t above, cand, at;
+    };
+    auto collect = [&](const uint32_t(&k)[kCached], const Span& sp) -> Marks {
+      uint32_t cm = 0u, abv = 0u;
 #pragma unroll
       for (int i = 0; i < kCached; ++i)
-        if (i < sp.per) cm |= (uint32_t)((k[i] & mask) == prefix) << i;
+        if (i < sp.per) {
+          cm |= (uint32_t)((k[i] & mask) == prefix) << i;
+          abv |= (uint32_t)((k[i] & mask) > prefix) << i;
+        }
       cm &= sp.live;
       uint32_t total;
       uint32_t slot = base + block_exclusive_scan<kThreads>(__popc(cm), scan_lds, &total);
+      const Marks marks{abv & sp.live, cm, slot};
 #pragma unroll
       for (int i = 0; i < kCached; ++i)
         if ((cm >> i) & 1u) cand[slot++] = k[i];
       base += total;
-    });
+      return marks;
+    };
+    if (keep_masks) {
+#pragma unroll
+      for (int r = 0; r < kMaskSR; ++r)
+        if (r < n_sr) {  // the same for every thread
+          uint32_t kk[kCached];
+          const Span sp = load_sr(r, kk);
+          const Marks mk = collect(kk, sp);
+          mark(r, 0) = mk.above;
+          mark(r, 1) = mk.cand;
+          mark(r, 2) = mk.at;
+        }
+    } else {
+      for_sr([&](const uint32_t(&k)[kCached], const Span& sp) { (void)collect(k, sp); });
+    }
   }
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
@@ -264,18 +301,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   const uint32_t thresh = prefix;
   const uint32_t needed_eq = remaining;  // >= 1 keys equal to thresh, lowest positions first
 
-  // 3. Output in position order (super-round, thread, bit).
+  // 3. Output in position order (super-round, thread, bit), from each thread's masks of keys > T
+  //    and == T.
   uint32_t gt_seen = 0u, eq_seen = 0u;  // over earlier super-rounds
-  for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
-    uint32_t gtm = 0u, eqm = 0u;
-#pragma unroll
-    for (int i = 0; i < kCached; ++i)
-      if (i < sp.per) {
-        gtm |= (uint32_t)(k[i] > thresh) << i;
-        eqm |= (uint32_t)(k[i] == thresh) << i;
-      }
-    gtm &= sp.live;
-    eqm &= sp.live;
+  auto emit_sr = [&](uint32_t gtm, uint32_t eqm, const Span& sp) {
     const uint32_t n_gt = __popc(gtm), n_eq = __popc(eqm);
     // One scan of both counts: per super-round each total is at most 32768, so the counts of keys
     // == T (low 16 bits) never carry into those of keys > T (high 16 bits).
@@ -294,7 +323,33 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
     }
     gt_seen += tot_gt;
     eq_seen += tot_eq;
-  });
+  };
+  if (keep_masks) {
+#pragma unroll
+    for (int r = 0; r < kMaskSR; ++r)
+      if (r < n_sr) {
+        // Keys above the threshold bin are kept; candidates are compared with T as `cand` holds them
+        // (this thread's, in bit order from cand_at[r]).
+        uint32_t gtm = mark(r, 0), eqm = 0u, at = mark(r, 2);
+        for (uint32_t m = mark(r, 1); m != 0u; m &= m - 1u) {
+          const uint32_t key = cand[at++], bit = m & (0u - m);
+          if (key > thresh) gtm |= bit;
+          else if (key == thresh) eqm |= bit;
+        }
+        emit_sr(gtm, eqm, span_of(r));
+      }
+  } else {
+    for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
+      uint32_t gtm = 0u, eqm = 0u;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i)
+        if (i < sp.per) {
+          gtm |= (uint32_t)(k[i] > thresh) << i;
+          eqm |= (uint32_t)(k[i] == thresh) << i;
+        }
+      emit_sr(gtm & sp.live, eqm & sp.live, sp);
+    });
+  }
 }
 
 }  // namespace

@@ -206,11 +206,13 @@ def test_select_topk_on_crafted_scores():
 
 @pytest.mark.parametrize("n,kind", [(40000, "normal"), (9000, "tied"), (70000, "tied"), (32768, "normal"),
                                     (5000, "two-values"), (20000, "cluster"), (12000, "outlier"), (9000, "inf"),
-                                    (6000, "huge")])
+                                    (6000, "huge"), (102400, "cluster"), (131072, "tied"), (140000, "normal")])
 def test_select_topk_paths(n, kind):
-    """Register-resident and re-read rows; threshold bucket resolved by pairwise ranking (normal), by
-    radix digits over its candidates (two-values, cluster, huge: a range too wide for float32 puts
-    every score in one bucket) or over all keys (tied, outlier: bucket larger than the LDS list)."""
+    """Register-resident rows (n <= 32768) and re-read rows: up to four super-rounds the output comes
+    from the masks kept by the candidate pass (40000, 70000, 102400), beyond that from a third read
+    (140000); threshold bucket resolved by radix digits over its candidates (normal, two-values,
+    cluster, huge: a range too wide for float32 puts every score in one bucket) or over all keys
+    (tied, outlier: bucket larger than the LDS list)."""
     rng = np.random.default_rng(n)
     B, H = 2, 3
     if kind == "normal":
