@@ -169,6 +169,8 @@ CombineArgs combine_args(const Ctx& c, int splits, void* out) {
   cb.out = out;
   cb.rows = c.d->batch * c.d->num_q_heads;
   cb.splits = splits;
+  cb.bf16 = c.d->dtype == PPSA_BF16 ? 1 : 0;
+  cb.head_dim = c.d->head_dim;
   return cb;
 }
 
@@ -211,10 +213,10 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
   int rc = finish(timed(select ? KERNEL_ATTN_FULL_SCORES : KERNEL_ATTN_FULL, c.stream, [&] {
     return c.plan.mfma ? launch_attn_mfma(a, mode, c.stream) : launch_attn(a, mode, c.d->dtype, c.d->head_dim, c.stream);
   }));
-  // A selection layer ranked by the logit sums merges its partials (bf16, head_dim 128) inside the
-  // selection launch: the two read disjoint inputs, and the merge then runs beside the top-k work
-  // on CUs it leaves idle instead of as a launch of its own.
-  const bool merge_in_select = select && !softmax && a.splits > 1 && c.d->dtype == PPSA_BF16 && c.d->head_dim == 128;
+  // A selection layer ranked by the logit sums merges its partials inside the selection launch: the
+  // two read disjoint inputs, and the merge then runs beside the top-k work on CUs it leaves idle
+  // instead of as a launch of its own.
+  const bool merge_in_select = select && !softmax && a.splits > 1;
   if (rc == PPSA_OK && !merge_in_select) rc = run_combine(c, a.splits, out);
   if (rc != PPSA_OK || !select) return rc;
   if (softmax) {

@@ -48,6 +48,8 @@ struct CombineArgs {
   void* out;                // [rows, D]
   int32_t rows;             // B * Hq
   int32_t splits;           // 1 .. kMaxSplitsPerUnit
+  int32_t bf16;             // output format when merged inside the selection launch: 1 bf16, 0 float32
+  int32_t head_dim;         // 64 or 128 (same)
 };
 
 // Softmax-weight selection scores (scores.hip): per (b, hq), M = max over live n of head_logits and
@@ -116,7 +118,7 @@ hipError_t launch_attn(const AttnArgs& a, int mode, int dtype, int head_dim, hip
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
-// One launch for a selection layer's top-k (a) and its merge pass (c; bf16, head_dim 128).
+// One launch for a selection layer's top-k (a) and its merge pass (c).
 hipError_t launch_select_merge(const SelectArgs& a, const CombineArgs& c, hipStream_t stream);
 
 // Launch timing (timing.hip). Kinds match the public PPSA_KERNEL_* values.

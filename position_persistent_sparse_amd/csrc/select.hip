@@ -89,16 +89,25 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
 
 // SHARED: one set per batch row, ranked by the sum of its KV heads' scores and written to every KV
 // head's row of idx (the head-shared selection variant); otherwise one set per (batch row, KV head).
-// MERGE: workgroups past the selection units merge the layer's split partials (bf16, head_dim 128),
-// one (batch row, query head) per wave; the merge and the selection read disjoint inputs and write
-// disjoint outputs, so they share the launch and the merge runs on CUs the selection leaves idle.
+// MERGE: workgroups past the selection units merge the layer's split partials, one (batch row, query
+// head) per wave; the merge and the selection read disjoint inputs and write disjoint outputs, so they
+// share the launch and the merge runs on CUs the selection leaves idle.
 template <bool CACHED, bool SHARED, bool MERGE>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, CombineArgs c) {
   if constexpr (MERGE) {
     const int units = SHARED ? a.batch : a.batch * a.kv_heads;
     if ((int)blockIdx.x >= units) {
       const int row = ((int)blockIdx.x - units) * kWaves + (int)threadIdx.x / kWave;
-      if (row < c.rows) merge::combine_row<uint16_t, 128>(c, row, (int)threadIdx.x % kWave);
+      const int ln = (int)threadIdx.x % kWave;
+      if (row < c.rows) {  // the output format is uniform across the launch
+        if (c.bf16) {
+          if (c.head_dim == 128) merge::combine_row<uint16_t, 128>(c, row, ln);
+          else merge::combine_row<uint16_t, 64>(c, row, ln);
+        } else {
+          if (c.head_dim == 128) merge::combine_row<float, 128>(c, row, ln);
+          else merge::combine_row<float, 64>(c, row, ln);
+        }
+      }
       return;
     }
   }
@@ -381,6 +390,7 @@ hipError_t launch_select_merge(const SelectArgs& a, const CombineArgs& c, hipStr
   if (a.batch <= 0) return hipSuccess;
   if (c.rows <= 0) return launch_select(a, stream);
   if (c.splits < 1 || c.splits > kMaxSplitsPerUnit) return hipErrorInvalidValue;
+  if (c.head_dim != 64 && c.head_dim != 128) return hipErrorInvalidValue;
   launch_select_kernel<true>(a, c, (c.rows + kWaves - 1) / kWaves, stream);
   return hipGetLastError();
 }

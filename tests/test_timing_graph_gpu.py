@@ -65,7 +65,7 @@ def test_launch_timing_counts_and_results(inputs):
     assert res["attn_full"][0] == n_f and res["attn_full_scores"][0] == n_x and res["attn_sparse"][0] == n_s
     assert res["select"][0] == n_x
     # Every layer of this shape is cut into several splits; a selection layer's merge runs inside its
-    # selection launch (bf16, head_dim 128), every other layer has a merge launch of its own.
+    # selection launch, every other layer has a merge launch of its own.
     assert res["combine"][0] == len(sched) - n_x
     assert res["dropped"] == 0
     for key in ppsa.KERNEL_KEYS:
