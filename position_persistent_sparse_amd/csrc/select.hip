@@ -5,17 +5,18 @@
 // with the highest attention score. Scores are float32; equal scores go to
 // the lower position. Output is the selected positions in ascending order.
 //
-// One 1024-thread workgroup per unit; the work is bound by instruction issue
-// on that one CU, so every step keeps the per-score work to a few
-// instructions and avoids per-score branches. Positions are taken in
+// One 1024-thread workgroup per unit; the work is bound by latency, barriers
+// and instruction issue on that one CU, so every step keeps the per-score
+// work to a few instructions and avoids per-score branches. Positions are taken in
 // super-rounds of up to 32768: in super-round r thread t owns per_r
 // contiguous positions (per_r = ceil(n_r / 1024) <= 32, loaded 16 bytes at a
 // time when aligned), so position order is (super-round, thread, bit). Each score maps to an
 // order-preserving 32-bit key (-0.0 folded onto +0.0): ranking floats is
 // ranking unsigned integers.
-//  1. Radix digit 1 (key bits 31..21) over all keys: an LDS histogram and a
-//     workgroup scan of the bins from the top give the bin holding the k-th
-//     largest key and how many keys lie above it.
+//  1. Radix digit 1 (key bits 31..21) over all keys: an LDS histogram (in
+//     four lane-interleaved copies, folded) and a workgroup scan of the bins
+//     from the top give the bin holding the k-th largest key and how many
+//     keys lie above it.
 //  2. The keys of that bin (the candidates) are copied to LDS (each thread's
 //     share placed by a workgroup scan of the per-thread counts); digits 2
 //     (bits 20..10) and 3 (bits 9..0) are resolved over the candidates only,
@@ -26,7 +27,9 @@
 //     prefix sum of the packed counts gives its first output slot, and it
 //     writes its kept positions in order by walking the set bits.
 // Rows of one super-round keep their keys in registers through all steps;
-// longer rows reload their super-rounds in each step.
+// longer rows reload their super-rounds in each step, except that rows of up
+// to four super-rounds take step 3 from masks kept by step 2 (two reads of
+// the scores instead of three).
 #include <math.h>
 
 #include "combine_row.h"
