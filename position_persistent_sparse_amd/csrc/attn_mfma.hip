@@ -73,7 +73,7 @@ __host__ __device__ constexpr int wave_region_floats(bool kt, int group) {
 }
 
 struct Tile {
-  uint4 k[2][4];    // [block][c]: K[row 16*blk + n][32c + 8g .. +8]
+  uint4 k[2][4];    // [block][c]: K[row 16*blk + n][32c + 8g .. +8] (sparse: once k_to_operand has run)
   uint4 v[2][4];    // [block][i]: V[row 16*blk + 4g + i][8n .. +8]
   uint32_t valid;   // bit 4*blk + i: row 16*blk + 4g + i is live
 };
