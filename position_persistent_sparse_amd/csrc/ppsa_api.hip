@@ -91,7 +91,7 @@ Plan make_plan(const ppsa_dims& d, int topk) {
     rows = ceil_div(units * topk, kSparseTargetGroups);
     rows = std::max<int64_t>(rows, ceil_div(topk, kMaxSplitsPerUnit));
     if ((int64_t)topk * kv_row_bytes <= kSingleSplitBytes) rows = topk;
-    const int cap = (p.mfma ? attn_mfma_max_sparse_rows() : attn_max_sparse_rows()) / granule * granule;
+    const int cap = p.mfma ? (1 << 20) : attn_max_sparse_rows() / granule * granule;
     p.sparse_rows = std::max(round_up(rows, granule), granule);
     if (p.sparse_rows > cap) {
       p.sparse_ok = false;
@@ -260,9 +260,9 @@ int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const 
   a.kslots = topk;
   a.splits = c.plan.sparse_splits;
   a.rows_per_split = c.plan.sparse_rows;
+  a.idx_vec = (topk % 4 == 0 && aligned(idx, 16)) ? 1 : 0;
   const int rc = finish(timed(KERNEL_ATTN_SPARSE, c.stream, [&] {
-    return c.plan.mfma ? launch_attn_mfma(a, MODE_SPARSE, c.stream)
-                       : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream);
+    return c.plan.mfma ? launch_attn_sparse(a, c.stream) : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream);
   }));
   return rc == PPSA_OK ? run_combine(c, a.splits, out) : rc;
 }

@@ -38,6 +38,7 @@ struct AttnArgs {
   int32_t splits, rows_per_split;
   float scale;              // logit scale (natural units)
   float scale_log2;         // scale * log2(e)
+  int32_t idx_vec;          // sparse: 1 when idx rows may be read 16 bytes at a time (kslots % 4 == 0, 16-byte aligned)
 };
 
 // Merge the partials of every (b, hq) into out[b, hq, :] (dtype of the cache).
@@ -92,12 +93,14 @@ hipError_t launch_coverage(const CoverageArgs& a, hipStream_t stream);
 int attn_rows_granule(int dtype, int head_dim);
 int attn_max_sparse_rows();
 
-// Matrix-core attention pass (bf16, head_dim 128, group <= 16).
+// Matrix-core full-attention pass (bf16, head_dim 128, group <= 16); sparse layers use launch_attn_sparse.
 bool attn_mfma_supported(int dtype, int head_dim, int group);
 int attn_mfma_rows_granule();
-int attn_mfma_max_sparse_rows();
 int attn_mfma_max_score_rows(int group);  // rows of one full-layer split (its scores are staged in LDS)
 hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream);
+// Sparse layer on the matrix cores (attn_sparse.hip, same contract as MODE_SPARSE): partials for
+// launch_combine, or the output itself when the unit has one split.
+hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t stream);
 // Largest group size the attention kernels take.
 constexpr int kMaxGroup = 16;
 // Most splits one unit may be cut into (the merge pass keeps one weight per split in LDS).
