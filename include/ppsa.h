@@ -55,7 +55,8 @@ typedef enum ppsa_status {
   PPSA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim, group size, dtype */
   PPSA_ERR_WORKSPACE = -3,   /* workspace smaller than ppsa_workspace_bytes() */
   PPSA_ERR_SCHEDULE = -4,    /* decode schedule: unknown kind, or sparse before any selection */
-  PPSA_ERR_HIP = -5          /* a HIP runtime call failed (kernel launch, event) */
+  PPSA_ERR_HIP = -5,         /* a HIP runtime call failed (kernel launch, event) */
+  PPSA_ERR_SCRATCH = -6      /* ppsa_decode_step_static: the step needs more than its static scratch */
 } ppsa_status;
 
 typedef enum ppsa_dtype { PPSA_F32 = 0, PPSA_BF16 = 1 } ppsa_dtype;
@@ -188,6 +189,31 @@ int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t
                         const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
                         int32_t select_mode, float coverage_tau, void* out, int32_t* idx, float* scores,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ppsa_decode_step (default selection: per KV head, logit sums) without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The call allocates nothing; its split partials and, when
+ * `scores` is NULL, its score array live in a static device array of 16 MiB
+ * built into the library (one per GPU the library runs on, held until the
+ * process ends; its device address is looked up once per device, with that
+ * device current, on the first call there). Arguments, layouts and results
+ * are those of ppsa_decode_step with the same plan, so outputs and indices
+ * are identical to it.
+ * The step needs 256-byte aligned regions of B*Hq*S*4 bytes (twice) and
+ * B*Hq*S*d*4 bytes for the partials (S <= 256 splits per unit), plus
+ * B*Hkv*Nmax*4 bytes for the scores when `scores` is NULL; a step that does
+ * not fit returns PPSA_ERR_SCRATCH before any HIP call (pass `scores`, or use
+ * ppsa_decode_step with a workspace). Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other threads)
+ * race and must not be issued; calls in one stream's order are safe. Nothing
+ * in the array needs clearing between calls. The stream must belong to the
+ * current device.
+ */
+int ppsa_decode_step_static(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+                            void* out, int32_t* idx, float* scores, void* stream);
 
 /*
  * Append one decode token to the caches (section 2, problem definition:

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libppsa.so")
 
 PPSA_OK, PPSA_ERR_INVALID_ARG, PPSA_ERR_UNSUPPORTED = 0, -1, -2
-PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP = -3, -4, -5
+PPSA_ERR_WORKSPACE, PPSA_ERR_SCHEDULE, PPSA_ERR_HIP, PPSA_ERR_SCRATCH = -3, -4, -5, -6
 PPSA_F32, PPSA_BF16 = 0, 1
 PPSA_FULL, PPSA_FULL_SELECT, PPSA_SPARSE = 0, 1, 2
 KIND_CODES = {"F": PPSA_FULL, "X": PPSA_FULL_SELECT, "S": PPSA_SPARSE}
@@ -65,13 +65,14 @@ def _load():
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
+    lib.ppsa_decode_step_static.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     lib.ppsa_timing_enable.argtypes = [i32]
     lib.ppsa_timing_read.argtypes = [vp, vp, i32, vp]
     lib.ppsa_timing_kernel_name.argtypes = [i32]
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
                  "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read",
-                 "ppsa_select_topk_ex", "ppsa_decode_step_ex"):
+                 "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -246,6 +247,31 @@ def decode_step(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, id
                                     _ptr(out), _ptr(idx),
                                     _ptr(scores), _ptr(ws), _workspace_nbytes(ws, q.device), _stream(q.device)),
            "ppsa_decode_step_ex")
+    return out, idx
+
+
+def decode_step_static(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=None, idx=None, scores=None,
+                       scale: float = 0.0, sched_codes=None):
+    """decode_step (default selection) on the library's static device scratch: no workspace. Output
+    tensors are still the caller's (allocated here when not given)."""
+    _check_tensors(q, k_cache, v_cache, seq_lens, layered=True)
+    dims = _dims_of(q, k_cache, scale, layered=True)
+    L = q.shape[0]
+    _require(len(schedule) == L, "schedule length must equal the layer count")
+    n_sel = sum(1 for k in schedule if k in ("X", PPSA_FULL_SELECT))
+    out = torch.empty_like(q) if out is None else out
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
+    if idx is None and n_sel:
+        idx = torch.empty((n_sel, dims.batch, dims.num_kv_heads, int(topk)), dtype=torch.int32, device=q.device)
+    if n_sel:
+        _check_buffer(idx, (n_sel, dims.batch, dims.num_kv_heads, int(topk)), torch.int32, q.device, "idx")
+    if scores is not None:
+        _check_buffer(scores, (n_sel, dims.batch, dims.num_kv_heads, dims.max_seq_len), torch.float32, q.device,
+                      "scores")
+    codes = schedule_codes(schedule) if sched_codes is None else sched_codes
+    _check(_lib.ppsa_decode_step_static(ctypes.byref(dims), L, codes, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(seq_lens), int(topk), _ptr(out), _ptr(idx), _ptr(scores),
+                                        _stream(q.device)), "ppsa_decode_step_static")
     return out, idx
 
 

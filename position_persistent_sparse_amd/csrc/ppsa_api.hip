@@ -9,9 +9,16 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ppsa_internal.h"
 #include "ppsa.h"
+
+// Device memory of ppsa_decode_step_static: a fixed array in the library's code object (one copy
+// per GPU the library runs on, held until the process ends), for callers that cannot allocate.
+// Host code never names it directly: its device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace ppsa {
 namespace {
@@ -74,7 +81,10 @@ int check_dims(const ppsa_dims* d) {
   return PPSA_OK;
 }
 
-Plan make_plan(const ppsa_dims& d, int topk) {
+// `variants`: also carve the regions the selection variants need (softmax-weight and coverage
+// selection); the default per-KV-head selection does without them. `score_buffer`: a score array
+// for selection layers whose caller passes none.
+Plan make_plan(const ppsa_dims& d, int topk, bool variants = true, bool score_buffer = true) {
   Plan p;
   p.mfma = use_mfma(d);
   const int granule = p.mfma ? attn_mfma_rows_granule() : attn_rows_granule(d.dtype, d.head_dim);
@@ -106,8 +116,8 @@ Plan make_plan(const ppsa_dims& d, int topk) {
   p.off_l = off; off = align_up(off + heads * p.max_splits * sizeof(float));
   p.off_o = off; off = align_up(off + heads * p.max_splits * d.head_dim * sizeof(float));
   p.off_scores = off;
-  off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * d.max_seq_len * sizeof(float));
-  if (topk > 0) {  // regions of the softmax-weight selection variant
+  if (score_buffer) off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * d.max_seq_len * sizeof(float));
+  if (topk > 0 && variants) {  // regions of the softmax-weight selection variant
     p.off_heads = off; off = align_up(off + heads * d.max_seq_len * sizeof(float));
     p.off_fm = off; off = align_up(off + heads * sizeof(float));
     p.off_fl = off; off = align_up(off + heads * sizeof(float));
@@ -268,18 +278,41 @@ int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const 
 }
 
 // Pointer and workspace checks common to the attention entry points.
+int check_io(const void* q, const void* k, const void* v, const int32_t* seq_lens, const void* out) {
+  if (!q || !k || !v || !seq_lens || !out) return PPSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
+    return PPSA_ERR_INVALID_ARG;
+  return PPSA_OK;
+}
+
 int check_tensors(const ppsa_dims* d, const void* q, const void* k, const void* v, const int32_t* seq_lens,
                   const void* out, const void* ws) {
-  if (!q || !k || !v || !seq_lens || !out || !ws) return PPSA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(ws, 16) ||
-      !aligned(seq_lens, 4))
-    return PPSA_ERR_INVALID_ARG;
   (void)d;
-  return PPSA_OK;
+  if (!ws || !aligned(ws, 16)) return PPSA_ERR_INVALID_ARG;
+  return check_io(q, k, v, seq_lens, out);
 }
 
 int check_topk(const ppsa_dims* d, int topk) {
   return (topk >= 1 && topk <= d->max_seq_len) ? PPSA_OK : PPSA_ERR_INVALID_ARG;
+}
+
+// Device address of `scratch` on the current device, looked up once per device (under a lock) with
+// that device current; the stored address is what kernels get, never the host-side symbol.
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices];
+
+int static_scratch(char** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return PPSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PPSA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = static_cast<char*>(g_scratch_addr[dev]);
+  return PPSA_OK;
 }
 
 }  // namespace
@@ -299,6 +332,7 @@ const char* ppsa_status_string(int status) {
     case PPSA_ERR_WORKSPACE: return "workspace too small";
     case PPSA_ERR_SCHEDULE: return "invalid decode schedule";
     case PPSA_ERR_HIP: return "HIP runtime call failed";
+    case PPSA_ERR_SCRATCH: return "needs more device memory than the static scratch holds";
     default: return "unknown status";
   }
 }
@@ -408,10 +442,17 @@ int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* s
                              0.0f, out, idx, scores, workspace, workspace_bytes, stream);
 }
 
-int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
-                        const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
-                        int32_t select_mode, float coverage_tau, void* out, int32_t* idx, float* scores,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace ppsa {
+namespace {
+
+// Argument checks of a decode step (no HIP call). On success sets the numbers of selection and
+// sparse layers.
+int check_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+               const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+               int32_t select_mode, float coverage_tau, const void* out, const int32_t* idx, const float* scores,
+               int* n_sel_out, int* n_sparse_out) {
   if (select_mode < PPSA_SELECT_PER_KV_HEAD || select_mode > PPSA_SELECT_COVERAGE) return PPSA_ERR_INVALID_ARG;
   if (select_mode == PPSA_SELECT_COVERAGE && !(coverage_tau >= 0.0f && coverage_tau < 1.0f))
     return PPSA_ERR_INVALID_ARG;  // also rejects NaN
@@ -430,23 +471,27 @@ int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t
     }
   }
   if (n_sel > 0 && (rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  *n_sel_out = n_sel;
+  *n_sparse_out = n_sparse;
   if (dims->batch == 0 || num_layers == 0) return PPSA_OK;
-  if ((rc = check_tensors(dims, q, k_cache, v_cache, seq_lens, out, workspace)) != PPSA_OK) return rc;
+  if ((rc = check_io(q, k_cache, v_cache, seq_lens, out)) != PPSA_OK) return rc;
   if (n_sel > 0 && (!idx || !aligned(idx, 4))) return PPSA_ERR_INVALID_ARG;
   if (scores && !aligned(scores, 4)) return PPSA_ERR_INVALID_ARG;
-  Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0), static_cast<char*>(workspace),
-        static_cast<hipStream_t>(stream)};
-  if (num_layers > n_sparse && !c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
-  if (n_sparse > 0 && !c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
-  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+  return PPSA_OK;
+}
 
+// The layers of a checked decode step, in order, on the workspace of plan `c`.
+int run_step(const Ctx& c, int32_t num_layers, const int32_t* schedule, const void* q, const void* k_cache,
+             const void* v_cache, const int32_t* seq_lens, int32_t topk, int32_t select_mode, float coverage_tau,
+             void* out, int32_t* idx, float* scores) {
+  const ppsa_dims* dims = c.d;
   const size_t eb = elem_bytes(dims->dtype);
   const size_t q_layer = (size_t)dims->batch * dims->num_q_heads * dims->head_dim * eb;
   const size_t kv_layer = (size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len * dims->head_dim * eb;
   const size_t idx_slot = (size_t)dims->batch * dims->num_kv_heads * (size_t)std::max(topk, 0);
   const size_t score_slot = (size_t)dims->batch * dims->num_kv_heads * dims->max_seq_len;
   (void)hipGetLastError();
-  int sel = -1;
+  int sel = -1, rc = PPSA_OK;
   for (int l = 0; l < num_layers; ++l) {
     const char* ql = static_cast<const char*>(q) + l * q_layer;
     const char* kl = static_cast<const char*>(k_cache) + l * kv_layer;
@@ -468,6 +513,47 @@ int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t
     if (rc != PPSA_OK) return rc;
   }
   return PPSA_OK;
+}
+
+}  // namespace
+}  // namespace ppsa
+
+extern "C" {
+
+int ppsa_decode_step_ex(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                        const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+                        int32_t select_mode, float coverage_tau, void* out, int32_t* idx, float* scores,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  int n_sel = 0, n_sparse = 0;
+  int rc = check_step(dims, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, select_mode, coverage_tau,
+                      out, idx, scores, &n_sel, &n_sparse);
+  if (rc != PPSA_OK || dims->batch == 0 || num_layers == 0) return rc;
+  if (!workspace || !aligned(workspace, 16)) return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0), static_cast<char*>(workspace),
+        static_cast<hipStream_t>(stream)};
+  if (num_layers > n_sparse && !c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
+  if (n_sparse > 0 && !c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
+  return run_step(c, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, select_mode, coverage_tau, out, idx,
+                  scores);
+}
+
+int ppsa_decode_step_static(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk,
+                            void* out, int32_t* idx, float* scores, void* stream) {
+  int n_sel = 0, n_sparse = 0;
+  int rc = check_step(dims, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, PPSA_SELECT_PER_KV_HEAD, 0.0f,
+                      out, idx, scores, &n_sel, &n_sparse);
+  if (rc != PPSA_OK || dims->batch == 0 || num_layers == 0) return rc;
+  // The default selection only: no regions for the selection variants.
+  Ctx c{dims, make_plan(*dims, n_sel > 0 ? topk : 0, false, n_sel > 0 && scores == nullptr), nullptr,
+        static_cast<hipStream_t>(stream)};
+  if (num_layers > n_sparse && !c.plan.full_ok) return PPSA_ERR_UNSUPPORTED;
+  if (n_sparse > 0 && !c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
+  if (c.plan.total > kStaticScratchBytes) return PPSA_ERR_SCRATCH;
+  if ((rc = static_scratch(&c.ws)) != PPSA_OK) return rc;
+  return run_step(c, num_layers, schedule, q, k_cache, v_cache, seq_lens, topk, PPSA_SELECT_PER_KV_HEAD, 0.0f, out,
+                  idx, scores);
 }
 
 }  // extern "C"

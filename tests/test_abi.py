@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 def test_abi_version_and_status_strings():
     assert ppsa.abi_version() == 1
     assert ppsa.status_string(0) == "ok"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         assert ppsa.status_string(code) not in ("ok", "unknown status")
     assert ppsa.status_string(99) == "unknown status"
 
@@ -201,3 +201,25 @@ def test_binding_rejects_mismatched_buffers():
         with pytest.raises(ValueError):
             ppsa._check_buffer(bad, (2, 3, 4), torch.int32, dev, "idx")
     assert ppsa._workspace_nbytes(torch.empty(10, dtype=torch.float32), dev) == 40
+
+
+def static_step(d, schedule, topk=16, idx=FAKE, scores=None, q=FAKE):
+    codes = ppsa.schedule_codes(schedule)
+    return LIB.ppsa_decode_step_static(ctypes.byref(d), len(schedule), codes, q, FAKE, FAKE, FAKE, topk, FAKE, idx,
+                                       scores, None)
+
+
+def test_static_scratch_step_validation():
+    """The no-workspace decode step checks its arguments, and its fit in the static scratch, before any
+    HIP call."""
+    d = dims()
+    assert static_step(d, "FFS") == ppsa.PPSA_ERR_SCHEDULE
+    assert static_step(d, "FFXS", topk=0) == ppsa.PPSA_ERR_INVALID_ARG
+    assert static_step(d, "FFXS", idx=None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert static_step(d, "FFXS", q=ODD) == ppsa.PPSA_ERR_INVALID_ARG
+    assert static_step(dims(batch=0), "FFXS") == ppsa.PPSA_OK
+    # 8 x 8 units x 300000 rows: the score array alone (76.8 MB) is past the 16 MiB scratch; with the
+    # caller's own score array the partials fit, and the call gets as far as the missing GPU.
+    big = dims(batch=8, q_heads=64, kv_heads=8, max_seq_len=300000)
+    assert static_step(big, "FFXS") == ppsa.PPSA_ERR_SCRATCH
+    assert ppsa.status_string(ppsa.PPSA_ERR_SCRATCH) != "unknown status"
