@@ -2,16 +2,30 @@
 
 Times whole decode steps (every layer of the schedule: full, full + top-k
 selection, sparse) through the C ABI entry point ppsa_decode_step, with all
-inputs resident in HBM, and prints one JSON line: achieved KV GB/s (the
-algorithmic K+V bytes a step must read, divided by the step time), step
-microseconds, the fraction of the 8 TB/s HBM peak, per-kernel durations from
-the library's launch timing (HIP events around each launch, on the stream the
-kernels run on), the roofline of the dominant kernel, the float64 CPU oracle
-timed over the same decode step on one host thread, and two comparison
-schedules over the same inputs (every layer full; a selection at every layer
-after the first two) with PPSA's speedup over each.
+inputs resident in HBM, and prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Headline (`value`, `ms_per_step`): the workload the metric is quoted on
+(LLaMA-3-8B GQA, 32K context), timed by the survey's protocol: K steps, each
+preceded (outside its HIP events) by a 1 GiB write that evicts the last-level
+cache and the L2s, reported as the median; `value` is the algorithmic K+V
+bytes of one step over that median. The same K steps back to back without
+eviction are reported beside it (`step_us_back_to_back`).
+
+The line also carries: per-kernel durations from the library's launch timing
+(HIP events around each launch, on the launch stream) and per-layer figures
+(attention launch plus its merge launch); the roofline of the dominant kernel
+against the 8 TB/s peak and against the read bandwidth this GPU reaches
+(`roofline.achievable`, from the read probe); the sparse kernel over its
+load-only twin; measurement probes (read ceiling, launch floor); a parity
+summary of the timed outputs on sampled (batch row, KV head) units against
+the float64 oracle; the oracle itself timed on the host cores
+(`cpu_baseline`); comparison schedules, selection variants and a multi-token
+decode on the headline workload; and `workloads`: the other four
+configurations timed the same way.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--workloads all|none|NAME,...]
+                    [--no-cpu-baseline] [--no-probes] [--no-parity] [--no-graph] [--no-comparison]
+                    [--no-multi-token] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -28,9 +42,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "PPSA decode-step attention µs and achieved KV GB/s (% of HBM peak)"
-EVICT_BYTES = 1 << 30  # written between per-step timings: larger than the last-level cache
-# Sources of the matrix-core attention kernel: the HBM traffic counted for it holds only while they are unchanged.
-ATTN_SOURCES = ("attn_mfma.hip", "attn_epilogue.h", "device_common.h", "ppsa_internal.h")
+EVICT_BYTES = 1 << 30  # read between per-step timings: larger than the last-level cache
+# Sources of the attention kernels: HBM traffic counted for a kernel holds only while they are unchanged.
+ATTN_SOURCES = ("attn_mfma.hip", "attn_sparse.hip", "mfma_tile.h", "sparse_gather.h", "attn_epilogue.h",
+                "device_common.h", "ppsa_internal.h")
+# Host threads the oracle may use: the GPU's share of the host (16 per GPU on the boxes this runs on).
+CPU_THREADS_CAP = 16
 
 
 def log(msg):
@@ -42,8 +59,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default=None)
+    p.add_argument("--workload", default=None, help="headline workload (default: the metric's configuration)")
+    p.add_argument("--workloads", default="all", help="other workloads to time: all, none or a comma list")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-probes", action="store_true")
+    p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB device copy (PMC calibration)")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (counter-collection runs)")
     p.add_argument("--no-comparison", action="store_true", help="skip the dense and select-every-layer schedules")
@@ -51,35 +71,89 @@ def parse():
     return p.parse_args()
 
 
-class OracleTimer:
-    """Times the float64 oracle over the whole decode step, one layer at a time as layers are generated."""
+def percentile(xs, p):
+    import numpy as np
 
-    def __init__(self, wl, seq_lens):
+    return float(np.percentile(np.asarray(xs), p))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(CPU_THREADS_CAP, n))
+
+
+class OracleTimer:
+    """Times the float64 oracle over the whole decode step, layer by layer as the layers are generated
+    (generation outside the timed calls), with the (batch row, KV head) units of a layer spread over a
+    pool of host threads (numpy releases the GIL in its array work; BLAS is held to one thread per
+    worker). Each unit keeps its own selection state across layers."""
+
+    def __init__(self, wl, seq_lens, threads):
+        import numpy as np
+
         import oracle
 
+        self.np = np
         self.oracle = oracle
         self.wl = wl
-        self.seq_lens = seq_lens
+        self.seq_lens = np.asarray(seq_lens)
+        self.threads = threads
         self.scale = oracle.default_scale(wl.head_dim)
-        self.sel = None
+        self.sel = {}
         self.secs = 0.0
+        self.pool = None
+        if threads > 1:
+            from concurrent.futures import ThreadPoolExecutor
+
+            self.pool = ThreadPoolExecutor(max_workers=threads)
+
+    def _unit(self, kind, q, K, V, b, h):
+        wl, g = self.wl, self.wl.group
+        out, sel, _ = self.oracle.decode_layer(kind, q[b:b + 1, h * g:(h + 1) * g], K[b:b + 1, h:h + 1],
+                                               V[b:b + 1, h:h + 1], self.seq_lens[b:b + 1], g, wl.topk,
+                                               self.scale, wl.dtype, self.sel.get((b, h)))
+        if sel is not None:
+            self.sel[(b, h)] = sel
+        return out
 
     def __call__(self, layer, q, K, V):
         import threadpoolctl
 
         kind = self.wl.schedule()[layer]
-        t0 = time.perf_counter()
+        units = [(b, h) for b in range(self.wl.batch) for h in range(self.wl.kv_heads)]
         with threadpoolctl.threadpool_limits(1):
-            _, self.sel, _ = self.oracle.decode_layer(kind, q, K, V, self.seq_lens, self.wl.group, self.wl.topk,
-                                                      self.scale, self.wl.dtype, self.sel)
-        self.secs += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            if self.pool is None:
+                for b, h in units:
+                    self._unit(kind, q, K, V, b, h)
+            else:
+                list(self.pool.map(lambda u: self._unit(kind, q, K, V, u[0], u[1]), units))
+            self.secs += time.perf_counter() - t0
+
+    def close(self):
+        if self.pool is not None:
+            self.pool.shutdown()
 
     def result(self, step_bytes):
-        return {"value": round(step_bytes / self.secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "step_us": round(self.secs * 1e6, 1),
-                "sample": f"the whole decode step ({self.wl.layers} layers, all {self.wl.batch * self.wl.kv_heads} "
-                          f"(batch, KV head) units) on 1 thread, {self.secs:.1f} s; inputs generated outside the "
-                          f"timed calls"}
+        wl = self.wl
+        return {"value": round(step_bytes / self.secs / 1e9, 4), "unit": "GB/s", "cores": self.threads,
+                "kind": "oracle", "step_us": round(self.secs * 1e6, 1), "cpu_model": cpu_model(),
+                "sample": f"the whole decode step ({wl.layers} layers, all {wl.batch * wl.kv_heads} (batch, KV "
+                          f"head) units, float64), {self.secs:.2f} s on {self.threads} host thread(s), units of a "
+                          f"layer spread over the threads; inputs generated outside the timed calls"}
 
 
 def attn_source_digest():
@@ -107,10 +181,470 @@ def measured_traffic(workload, kernel_key):
     return int(round(b)), os.path.basename(path)
 
 
-def percentile(xs, p):
-    import numpy as np
+class Bench:
+    """Shared GPU state: the stream, an eviction buffer, a sink for probes."""
 
-    return float(np.percentile(np.asarray(xs), p))
+    def __init__(self, args):
+        import torch
+
+        import position_persistent_sparse_amd as ppsa
+
+        self.torch = torch
+        self.ppsa = ppsa
+        self.args = args
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.sink = torch.zeros(16, dtype=torch.int32, device=self.dev)
+        self.scratch = None
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def evict(self, i):
+        """A plain read of 1 GiB: the last-level cache and the L2s then hold clean, unrelated lines (a write
+        would leave dirty lines whose write-back the next step would pay)."""
+        if self.scratch is None:
+            self.scratch = self.torch.ones(EVICT_BYTES, dtype=self.torch.uint8, device=self.dev)
+        # Twice: the GPU is still reading when the host enqueues the step, so no idle gap falls inside the
+        # step's events.
+        self.ppsa.probe_read(self.scratch, False, self.sink)
+        self.ppsa.probe_read(self.scratch, False, self.sink)
+
+    def graph_time(self, fn, calls, replays=3):
+        """µs per call of `calls` calls captured in one HIP graph and replayed back to back (no host work
+        between the launches)."""
+        torch = self.torch
+        side = torch.cuda.Stream(self.dev)
+        side.wait_stream(self.stream)
+        with torch.cuda.stream(side):
+            fn(0)
+        self.stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(calls):
+                fn(i)
+        graph.replay()
+        us = self.time_loop(lambda i: graph.replay(), replays) / calls
+        del graph
+        return us
+
+    def time_loop(self, fn, reps):
+        """Back-to-back: µs per call over `reps` calls, bracketed by events on the launch stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0, e1 = self.ev(), self.ev()
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def time_each(self, fn, reps, evict=False):
+        """µs of each call, each bracketed by its own events (eviction outside them when asked); one
+        synchronisation before and after the whole loop."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        pairs = []
+        for i in range(reps):
+            if evict:
+                self.evict(i)
+            e0, e1 = self.ev(), self.ev()
+            e0.record(self.stream)
+            fn(i)
+            e1.record(self.stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in pairs]
+
+    def probes(self):
+        """The read ceiling of this GPU, the fixed cost of a launch, and the read of a sparse layer's size."""
+        torch, ppsa = self.torch, self.ppsa
+        res = {}
+        n = 4 << 30
+        buf = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        buf.fill_(1)
+        for nt in (True, False):
+            ppsa.probe_read(buf, nt, self.sink)
+            us = self.time_loop(lambda i: ppsa.probe_read(buf, nt, self.sink), 5)
+            res["read_4GiB_" + ("nontemporal" if nt else "plain")] = {"us": round(us, 1),
+                                                                    "GB_per_s": round(n / us / 1e3, 1)}
+        # 64 MiB reads (a sparse layer's K+V bytes at the LLaMA-3-8B 32K shape), each from a new part of the
+        # 4 GiB buffer, so that none is served by the last-level cache.
+        part = 64 << 20
+        views = [buf[i * part:(i + 1) * part] for i in range(n // part)]
+        us = self.graph_time(lambda i: ppsa.probe_read(views[i % len(views)], True, self.sink), len(views))
+        res["read_64MiB_nontemporal"] = {"us": round(us, 2), "GB_per_s": round(part / us / 1e3, 1),
+                                         "timing": "back to back in a captured graph"}
+        del views, buf
+        for groups, threads in ((512, 256), (64, 512)):
+            key = f"empty_kernel_{groups}x{threads}"
+            rec = {"us_per_launch_graph": round(self.graph_time(lambda i: ppsa.probe_empty(groups, threads, self.sink),
+                                                                100), 2),
+                   "us_per_launch_python_loop": round(
+                       self.time_loop(lambda i: ppsa.probe_empty(groups, threads, self.sink), 200), 2)}
+            res[key] = rec
+        torch.cuda.synchronize()
+        return res
+
+
+class WorkloadRun:
+    """One workload: inputs resident on the GPU, the step timed, kernels and layers timed, parity sampled."""
+
+    def __init__(self, bench, wl, headline, oracle_threads):
+        import numpy as np
+
+        import synth
+        from synth import torch_io
+
+        self.b = bench
+        self.wl = wl
+        self.np = np
+        self.synth = synth
+        torch, ppsa = bench.torch, bench.ppsa
+        self.gen = synth.Generator(wl)
+        self.sched = wl.schedule()
+        self.n_sel = self.sched.count("X")
+        self.units = self._sample_units(4 if headline else 2)
+        self.timer = None
+        if oracle_threads:
+            self.timer = OracleTimer(wl, self.gen.seq_lens, oracle_threads)
+        log(f"generating {wl.name}: {wl.layers} layers, B={wl.batch}, Hq={wl.q_heads}, Hkv={wl.kv_heads}, "
+            f"N={wl.max_len}, k={wl.topk}, {wl.dtype}"
+            + ("" if self.timer is None else f"; timing the oracle per layer on {oracle_threads} thread(s)"))
+        t0 = time.time()
+        keep = None if bench.args.no_parity else set(range(wl.layers))
+        self.q, self.k, self.v, self.lens, self.host = torch_io.upload(
+            wl, self.gen, bench.dev, keep_layers=keep if keep is not None else set(),
+            keep_units=self.units, visit=self.timer)
+        if self.timer is not None:
+            self.timer.close()
+        torch.cuda.synchronize()
+        log(f"{wl.name}: inputs resident after {time.time() - t0:.1f} s")
+        self.dims = ppsa.make_dims(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.max_len,
+                                   torch_io.torch_dtype(wl))
+        self.ws = ppsa.alloc_workspace(self.dims, wl.topk, bench.dev)
+        self.out = torch.empty_like(self.q)
+        self.idx = torch.empty((max(self.n_sel, 1), wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32,
+                               device=bench.dev)
+        self.codes = ppsa.schedule_codes(self.sched)
+        self.step_bytes = synth.step_kv_bytes(wl, self.gen.seq_lens)
+
+    def _sample_units(self, count):
+        wl = self.wl
+        units = [(b, h) for b in range(wl.batch) for h in range(wl.kv_heads)]
+        if len(units) <= count:
+            return units
+        stride = len(units) / count
+        return [units[int(i * stride + stride / 2)] for i in range(count)]
+
+    def step(self, *_):
+        self.b.ppsa.decode_step(self.sched, self.q, self.k, self.v, self.lens, self.wl.topk, out=self.out,
+                                idx=self.idx if self.n_sel else None, workspace=self.ws, sched_codes=self.codes)
+
+    def free(self):
+        del self.q, self.k, self.v, self.ws, self.out, self.idx, self.host
+        self.b.torch.cuda.empty_cache()
+
+    def time_steps(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        evicted = self.b.time_each(self.step, steps, evict=True)
+        b2b = self.b.time_loop(self.step, steps)
+        return evicted, b2b
+
+    def kernel_times(self, steps):
+        """Per-kernel durations from the library's launch timing over `steps` steps."""
+        ppsa = self.b.ppsa
+        launches_per_step = 2 * len(self.sched) + self.n_sel
+        ppsa.timing_enable(launches_per_step * steps)
+        try:
+            us = self.b.time_loop(self.step, steps)
+            timed = ppsa.timing_read()
+        finally:
+            ppsa.timing_enable(0)
+        kernels = {}
+        for key in ppsa.KERNEL_KEYS:
+            n, ms = timed[key]
+            if n:
+                kernels[key] = {"launches_per_step": round(n / steps, 2), "us_per_launch": round(ms * 1e3 / n, 2),
+                                "us_per_step": round(ms * 1e3 / steps, 1)}
+        wl, lens = self.wl, self.gen.seq_lens
+        self.layer_bytes = {"attn_full": self.synth.layer_kv_bytes(wl, "F", lens),
+                            "attn_full_scores": self.synth.layer_kv_bytes(wl, "X", lens),
+                            "attn_sparse": self.synth.layer_kv_bytes(wl, "S", lens)}
+        for key, nbytes in self.layer_bytes.items():
+            if key in kernels:
+                gb = nbytes / (kernels[key]["us_per_launch"] * 1e-6) / 1e9
+                kernels[key].update({"kv_bytes_per_launch": nbytes, "GB_per_s": round(gb, 1),
+                                     "hbm_frac": round(gb / HBM_PEAK_GBS, 4)})
+        return kernels, us
+
+    def layer_times(self, kernels):
+        """Per layer kind: the attention launch plus the merge launch that follows it (when the layer's
+        units have several splits), from the event brackets, and the layers timed back to back through
+        the single-layer entry points."""
+        ppsa = self.b.ppsa
+        n_f, n_s = self.sched.count("F"), self.sched.count("S")
+        n_comb = kernels.get("combine", {}).get("launches_per_step", 0)
+        comb_us = kernels.get("combine", {}).get("us_per_launch", 0.0)
+        full_merged = n_comb in (n_f, n_f + n_s) and n_f > 0
+        sparse_merged = n_comb in (n_s, n_f + n_s) and n_s > 0
+        res = {}
+        if "attn_full" in kernels:
+            us = kernels["attn_full"]["us_per_launch"] + (comb_us if full_merged else 0.0)
+            res["full_layer"] = {"events_us": round(us, 2), "merge_launch": full_merged,
+                                 "GB_per_s": round(self.layer_bytes["attn_full"] / us / 1e3, 1)}
+        if "attn_full_scores" in kernels and "select" in kernels:
+            us = kernels["attn_full_scores"]["us_per_launch"] + kernels["select"]["us_per_launch"]
+            res["selection_layer"] = {"events_us": round(us, 2), "note": "attention + score write, then top-k "
+                                      "(whose launch also merges the layer's partials)"}
+        if "attn_sparse" in kernels:
+            us = kernels["attn_sparse"]["us_per_launch"] + (comb_us if sparse_merged else 0.0)
+            res["sparse_layer"] = {"events_us": round(us, 2), "merge_launch": sparse_merged,
+                                   "GB_per_s": round(self.layer_bytes["attn_sparse"] / us / 1e3, 1),
+                                   "hbm_frac": round(self.layer_bytes["attn_sparse"] / us / 1e3 / HBM_PEAK_GBS, 4)}
+            # The sparse layers of a step back to back through ppsa_sparse_attn (kernel + merge launch).
+            s_layers = [layer for layer, kind in enumerate(self.sched) if kind == "S"]
+            sel_of = {}
+            sel = -1
+            for layer, kind in enumerate(self.sched):
+                if kind == "X":
+                    sel += 1
+                sel_of[layer] = sel
+            outs = self.out
+
+            def one(i):
+                layer = s_layers[i % len(s_layers)]
+                ppsa.sparse_attn(self.q[layer], self.k[layer], self.v[layer], self.lens, self.idx[sel_of[layer]],
+                                 out=outs[layer], workspace=self.ws)
+
+            self.step()
+            us = self.b.graph_time(one, len(s_layers))
+            res["sparse_layer"]["back_to_back_us"] = round(us, 2)
+            res["sparse_layer"]["back_to_back_GB_per_s"] = round(self.layer_bytes["attn_sparse"] / us / 1e3, 1)
+            res["sparse_layer"]["back_to_back_timing"] = "the step's sparse layers through ppsa_sparse_attn " \
+                                                         "(kernel and merge launch), captured in a graph"
+        return res
+
+    def gather_twin(self):
+        """The sparse kernel's load-only twin over this step's sparse layers (event-bracketed like the
+        launch timing)."""
+        ppsa = self.b.ppsa
+        s_layers = [layer for layer, kind in enumerate(self.sched) if kind == "S"]
+        if not s_layers or self.wl.dtype != "bf16" or self.wl.head_dim != 128:
+            return None
+        sel_of, sel = {}, -1
+        for layer, kind in enumerate(self.sched):
+            if kind == "X":
+                sel += 1
+            sel_of[layer] = sel
+        self.step()
+
+        def one(i):
+            layer = s_layers[i % len(s_layers)]
+            ppsa.probe_gather(self.k[layer], self.v[layer], self.lens, self.idx[sel_of[layer]], self.wl.q_heads,
+                              self.b.sink)
+
+        us = self.b.graph_time(one, 2 * len(s_layers))
+        nbytes = self.synth.layer_kv_bytes(self.wl, "S", self.gen.seq_lens)
+        return {"us_per_launch": round(us, 2), "GB_per_s": round(nbytes / us / 1e3, 1), "kv_bytes_per_launch": nbytes,
+                "timing": "back to back over the step's sparse layers (each its own K/V, as in the step), "
+                          "captured in a graph: from the previous launch's end to this one's"}
+
+    def parity(self):
+        """The timed step's outputs on the sampled units against the float64 oracle: per layer kind the
+        max abs error, the relative L2 error, and at selection layers the band rule (positions inside the
+        1e-3 band counted). Sparse layers are evaluated on the GPU's own selection."""
+        if self.b.args.no_parity:
+            return None
+        import oracle
+        from oracle import compare
+        from synth import torch_io
+
+        np, wl = self.np, self.wl
+        self.step()
+        self.b.torch.cuda.synchronize()
+        out = torch_io.from_torch(self.out)
+        out = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if wl.dtype == "bf16" \
+            else out.astype(np.float64)
+        idx = self.idx.cpu().numpy()
+        scale = oracle.default_scale(wl.head_dim)
+        g = wl.group
+        acc = {k: {"max_abs": 0.0, "err2": 0.0, "ref2": 0.0, "layers": 0} for k in ("F", "X", "S")}
+        band_pos, sel_ok = 0, True
+        sel_i = -1
+        for layer, kind in enumerate(self.sched):
+            if kind == "X":
+                sel_i += 1
+            for (b, h) in self.units:
+                qg, kb, vb = self.host[layer][(b, h)]
+                n = int(self.gen.seq_lens[b])
+                selection = idx[sel_i, b, h][None, None] if kind == "S" else None
+                want, _, oscores = oracle.decode_layer(kind, qg[None], kb[None, None], vb[None, None],
+                                                       np.array([n]), g, wl.topk, scale, wl.dtype, selection)
+                got = out[layer, b, h * g:(h + 1) * g]
+                err = np.abs(got - want[0])
+                a = acc[kind]
+                a["max_abs"] = max(a["max_abs"], float(err.max()))
+                a["err2"] += float(np.sum(err ** 2))
+                a["ref2"] += float(np.sum(want[0] ** 2))
+                if kind == "X":
+                    ok, _, inband = compare.check_selection_band(idx[sel_i, b, h], oscores[0, 0], n, wl.topk)
+                    sel_ok &= ok
+                    band_pos += inband
+            acc[kind]["layers"] += 1
+        tol = 1e-5 if wl.dtype == "f32" else 2e-2
+        res = {"units": [list(u) for u in self.units], "tolerance_max_abs": tol, "selection_band_rule_ok": sel_ok,
+               "band_positions": band_pos}
+        ok = sel_ok
+        for kind, name in (("F", "full"), ("X", "selection"), ("S", "sparse")):
+            a = acc[kind]
+            if a["layers"]:
+                rel = (a["err2"] / a["ref2"]) ** 0.5 if a["ref2"] > 0 else 0.0
+                res[name] = {"layers": a["layers"], "max_abs": float(f"{a['max_abs']:.3e}"),
+                             "rel_l2": float(f"{rel:.3e}")}
+                ok &= a["max_abs"] <= tol
+        res["ok"] = bool(ok)
+        return res
+
+    def summary(self, steps, warmup, with_twin=True):
+        """Step, kernel and layer timings plus parity: the record of one workload."""
+        evicted, b2b = self.time_steps(steps, warmup)
+        med = percentile(evicted, 50)
+        kernels, instrumented = self.kernel_times(steps)
+        sel_us = kernels.get("select", {}).get("us_per_step", 0.0)
+        if "attn_full_scores" in kernels and "attn_full" in kernels:
+            sel_us += self.n_sel * (kernels["attn_full_scores"]["us_per_launch"] - kernels["attn_full"]["us_per_launch"])
+        rec = {"workload": self.wl.name, "layers": self.wl.layers, "batch": self.wl.batch,
+               "q_heads": self.wl.q_heads, "kv_heads": self.wl.kv_heads, "head_dim": self.wl.head_dim,
+               "seq_len": self.wl.max_len, "seq_lens": "ragged " + str(self.gen.seq_lens.tolist())
+               if self.wl.ragged else self.wl.max_len, "topk": self.wl.topk, "dtype": self.wl.dtype,
+               "schedule": "".join(self.sched), "kv_bytes_per_step": self.step_bytes,
+               "step_us": round(med, 1),
+               "step_us_evicted": {"median": round(med, 1), "p10": round(percentile(evicted, 10), 1),
+                                   "p90": round(percentile(evicted, 90), 1)},
+               "step_us_back_to_back": round(b2b, 1),
+               "GB_per_s": round(self.step_bytes / med / 1e3, 1),
+               "hbm_frac": round(self.step_bytes / med / 1e3 / HBM_PEAK_GBS, 4),
+               "step_us_with_launch_timing": round(instrumented, 1),
+               "selection_overhead_frac": round(sel_us / med, 4),
+               "kernels": kernels, "layers_timed": self.layer_times(kernels)}
+        if with_twin:
+            twin = self.gather_twin()
+            if twin and "attn_sparse" in kernels:
+                twin["sparse_kernel_over_twin"] = round(kernels["attn_sparse"]["us_per_launch"] / twin["us_per_launch"], 3)
+            rec["gather_twin"] = twin
+        rec["parity"] = self.parity()
+        return rec
+
+
+def comparison_schedules(run, steps, base_us):
+    """Dense and select-every-layer schedules, and the selection variants, over the same inputs."""
+    ppsa, torch, wl = run.b.ppsa, run.b.torch, run.wl
+    comparison = {}
+    for name, sch in (("dense", ["F"] * wl.layers), ("select_every_layer", ["F", "F"] + ["X"] * (wl.layers - 2))):
+        c_codes = ppsa.schedule_codes(sch)
+        n_x = sch.count("X")
+        c_idx = torch.empty((max(n_x, 1), wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32, device=run.b.dev)
+
+        def c_step(*_):
+            ppsa.decode_step(sch, run.q, run.k, run.v, run.lens, wl.topk, out=run.out, idx=c_idx if n_x else None,
+                             workspace=run.ws, sched_codes=c_codes)
+
+        c_step()
+        us = run.b.time_loop(c_step, steps)
+        comparison[name] = {"schedule": "".join(sch), "step_us": round(us, 1), "ppsa_speedup": round(us / base_us, 3)}
+        del c_idx
+
+    def overlap(a, b):
+        """Mean over (selection layer, batch row, KV head) of the fraction of set a also in set b."""
+        fr = []
+        for s in range(a.shape[0]):
+            for bb in range(a.shape[1]):
+                for hh in range(a.shape[2]):
+                    x, y = a[s, bb, hh], b[s, bb, hh]
+                    x = x[x >= 0]
+                    if x.numel():
+                        fr.append(float(torch.isin(x, y[y >= 0]).float().mean()))
+        return round(sum(fr) / max(len(fr), 1), 4)
+
+    run.step()
+    torch.cuda.synchronize()
+    idx_default = run.idx.clone()
+    for mode, extra in (("shared", {}), ("softmax", {}), ("coverage", {"coverage_tau": 0.8})):
+        def v_step(*_):
+            ppsa.decode_step(run.sched, run.q, run.k, run.v, run.lens, wl.topk, out=run.out, idx=run.idx,
+                             workspace=run.ws, sched_codes=run.codes, select_mode=mode, **extra)
+
+        v_step()
+        us = run.b.time_loop(v_step, steps)
+        rec = {"schedule": "".join(run.sched), "select_mode": mode, "step_us": round(us, 1),
+               "ppsa_speedup": round(us / base_us, 3), "overlap_with_default_set": overlap(idx_default, run.idx)}
+        if mode == "coverage":
+            kept = (run.idx >= 0).sum(dim=-1).float()
+            rec.update({"tau": 0.8, "cap": wl.topk, "kept_per_unit": {"mean": round(float(kept.mean()), 1),
+                                                                       "min": int(kept.min()), "max": int(kept.max())}})
+        comparison[mode + "_selection"] = rec
+    run.step()
+    return comparison
+
+
+def graph_replay(run, steps):
+    torch = run.b.torch
+    try:
+        side = torch.cuda.Stream(run.b.dev)
+        side.wait_stream(run.b.stream)
+        with torch.cuda.stream(side):
+            run.step()
+        run.b.stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run.step()
+        graph.replay()
+        us = run.b.time_loop(lambda i: graph.replay(), steps)
+        del graph
+        return round(us, 1)
+    except Exception as exc:  # reported, never fatal: the eager step is the measurement
+        log(f"graph replay not measured: {exc}")
+        return None
+
+
+def multi_token(run, steps):
+    """T tokens, each appending its K/V rows and then running the step, each batch row starting T rows short
+    of its length so that every token has room (last: it writes cache rows)."""
+    torch, ppsa, wl = run.b.torch, run.b.ppsa, run.wl
+    T = steps
+    lens_mt = torch.clamp(run.lens - T, min=0).to(torch.int32)
+    kn = torch.randn((wl.layers, wl.batch, wl.kv_heads, wl.head_dim), device=run.b.dev).to(run.k.dtype)
+    vn = torch.randn_like(kn)
+
+    def token(*_):
+        ppsa.append_kv(kn, vn, run.k, run.v, lens_mt)
+        ppsa.decode_step(run.sched, run.q, run.k, run.v, lens_mt, wl.topk, out=run.out, idx=run.idx,
+                         workspace=run.ws, sched_codes=run.codes)
+
+    us = run.b.time_loop(token, T)
+    ok = bool(torch.equal(lens_mt, torch.clamp(run.lens - T, min=0).to(torch.int32) + T))
+    return {"tokens": T, "us_per_token": round(us, 1), "start_lengths": "each batch row T rows short of its length",
+            "lengths_grew_by_tokens": ok}
+
+
+def one_thread_oracle(wl):
+    """The oracle over the whole step of a small workload on one host thread (baseline plan: C1 and C2)."""
+    import synth
+
+    gen = synth.Generator(wl)
+    timer = OracleTimer(wl, gen.seq_lens, 1)
+    kb = vb = None
+    for layer in range(wl.layers):
+        kb, vb = gen.kv(layer, kb, vb)
+        timer(layer, gen.q(layer), kb, vb)
+    nbytes = synth.step_kv_bytes(wl, gen.seq_lens)
+    return {"value": round(nbytes / timer.secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "step_us": round(timer.secs * 1e6, 1)}
 
 
 def main():
@@ -120,287 +654,81 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import position_persistent_sparse_amd as ppsa
     import synth
-    from synth import torch_io
 
+    bench = Bench(args)
+    probes = None
+    if not args.no_probes:
+        probes = bench.probes()
+        log("probes: " + json.dumps(probes))
+
+    # Headline workload.
     wl = synth.WORKLOADS[args.workload or synth.BENCH_WORKLOAD]
-    dev = torch.device("cuda:0")
-    gen = synth.Generator(wl)
-    timer = None if args.no_cpu_baseline else OracleTimer(wl, gen.seq_lens)
-    log(f"generating {wl.name}: {wl.layers} layers, B={wl.batch}, Hq={wl.q_heads}, Hkv={wl.kv_heads}, "
-        f"N={wl.max_len}, k={wl.topk}, {wl.dtype}" + ("" if timer is None else "; timing the oracle per layer"))
-    t0 = time.time()
-    q, k, v, lens, _ = torch_io.upload(wl, gen, dev, keep_layers=set(), visit=timer)
-    torch.cuda.synchronize()
-    log(f"inputs resident on {torch.cuda.get_device_name(dev)} after {time.time() - t0:.1f} s")
-
-    sched = wl.schedule()
-    n_sel = sched.count("X")
-    dims = ppsa.make_dims(wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim, wl.max_len, torch_io.torch_dtype(wl))
-    ws = ppsa.alloc_workspace(dims, wl.topk, dev)
-    out = torch.empty_like(q)
-    idx = torch.empty((n_sel, wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32, device=dev)
-    codes = ppsa.schedule_codes(sched)
-    stream = torch.cuda.current_stream(dev)
-    step_bytes = synth.step_kv_bytes(wl, gen.seq_lens)
-
-    def step():
-        ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes)
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # 1. The timed region: K back-to-back steps.
-    start, end = ev(), ev()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of peak)")
-
-    # 2. Per-step times, each step preceded (outside its events) by a 1 GiB write that evicts the caches.
-    scratch = torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
-    per_step = []
-    for i in range(args.steps):
-        scratch.fill_(i & 0xFF)
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_step.append(e0.elapsed_time(e1) * 1e3)
-    del scratch
-    log(f"evicted steps: median {percentile(per_step, 50):.1f} us")
-
-    # 3. Per-kernel durations: the library's launch timing (two HIP events around each launch).
-    launches_per_step = 2 * len(sched) + n_sel
-    ppsa.timing_enable(launches_per_step * args.steps)
-    try:
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        timed = ppsa.timing_read()
-    finally:
-        ppsa.timing_enable(0)
-    instrumented_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    kernels = {}
-    for key in ppsa.KERNEL_KEYS:
-        n, ms = timed[key]
-        if n:
-            kernels[key] = {"launches_per_step": round(n / args.steps, 2), "us_per_launch": round(ms * 1e3 / n, 2),
-                            "us_per_step": round(ms * 1e3 / args.steps, 1)}
-    layer_bytes = {"attn_full": synth.layer_kv_bytes(wl, "F", gen.seq_lens),
-                   "attn_full_scores": synth.layer_kv_bytes(wl, "X", gen.seq_lens),
-                   "attn_sparse": synth.layer_kv_bytes(wl, "S", gen.seq_lens)}
-    for key, b in layer_bytes.items():
-        if key in kernels:
-            gb = b / (kernels[key]["us_per_launch"] * 1e-6) / 1e9
-            kernels[key].update({"kv_bytes_per_launch": b, "GB_per_s": round(gb, 1),
-                                 "hbm_frac": round(gb / HBM_PEAK_GBS, 4)})
-
-    # 4. The same step replayed from a captured HIP graph.
-    graph_us = None
-    try:
-        if args.no_graph:
-            raise RuntimeError("skipped (--no-graph)")
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            step()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        graph_us = round(e0.elapsed_time(e1) * 1e3 / args.steps, 1)
-        del graph
-    except Exception as exc:  # reported, never fatal: the eager step is the measurement
-        log(f"graph replay not measured: {exc}")
-
-    # 5. Comparison schedules over the same inputs: every layer full (the dense decode step TidalDecode
-    # is measured against) and a selection at every layer after the first two.
-    comparison = {}
-    for name, sch in (("dense", ["F"] * wl.layers), ("select_every_layer", ["F", "F"] + ["X"] * (wl.layers - 2))):
-        if args.no_comparison or wl.layers < 3:
-            break
-        c_codes = ppsa.schedule_codes(sch)
-        n_x = sch.count("X")
-        c_idx = torch.empty((max(n_x, 1), wl.batch, wl.kv_heads, wl.topk), dtype=torch.int32, device=dev)
-
-        def c_step():
-            ppsa.decode_step(sch, q, k, v, lens, wl.topk, out=out, idx=c_idx if n_x else None, workspace=ws,
-                             sched_codes=c_codes)
-
-        c_step()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            c_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.steps
-        comparison[name] = {"schedule": "".join(sch), "step_us": round(us, 1),
-                            "ppsa_speedup": round(us / (ms_per_step * 1e3), 3)}
-        del c_idx
-    def overlap(a, b):
-        """Mean over (selection layer, batch row, KV head) of the fraction of set a also in set b."""
-        fr = []
-        for sel_i in range(a.shape[0]):
-            for bb in range(a.shape[1]):
-                for hh in range(a.shape[2]):
-                    x, y = a[sel_i, bb, hh], b[sel_i, bb, hh]
-                    x = x[x >= 0]
-                    if x.numel():
-                        fr.append(float(torch.isin(x, y[y >= 0]).float().mean()))
-        return round(sum(fr) / max(len(fr), 1), 4)
-
-    if not args.no_comparison and n_sel:
-        step()
-        torch.cuda.synchronize()
-        idx_default = idx.clone()
-        # Selection variant: one set per batch row over all of its query heads (same schedule and inputs).
-        def shared_step():
-            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
-                             select_mode="shared")
-
-        shared_step()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            shared_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.steps
-        comparison["shared_selection"] = {"schedule": "".join(sched), "select_mode": "shared", "step_us": round(us, 1),
-                                          "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
-                                          "overlap_with_default_set": overlap(idx_default, idx)}
-
-        def softmax_step():
-            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
-                             select_mode="softmax")
-
-        softmax_step()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            softmax_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.steps
-        comparison["softmax_selection"] = {"schedule": "".join(sched), "select_mode": "softmax",
-                                           "step_us": round(us, 1), "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
-                                           "overlap_with_default_set": overlap(idx_default, idx)}
-
-        # Coverage budget instead of a fixed k (capped at k): prune the lowest-mass tail past tau.
-        tau = 0.8
-
-        def coverage_step():
-            ppsa.decode_step(sched, q, k, v, lens, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes,
-                             select_mode="coverage", coverage_tau=tau)
-
-        coverage_step()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(args.steps):
-            coverage_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / args.steps
-        kept = (idx >= 0).sum(dim=-1).float()
-        comparison["coverage_selection"] = {"schedule": "".join(sched), "select_mode": "coverage", "tau": tau,
-                                            "cap": wl.topk, "step_us": round(us, 1),
-                                            "ppsa_speedup": round(us / (ms_per_step * 1e3), 3),
-                                            "kept_per_unit": {"mean": round(float(kept.mean()), 1),
-                                                              "min": int(kept.min()), "max": int(kept.max())}}
-    if comparison:
+    threads = 0 if args.no_cpu_baseline else host_threads()
+    run = WorkloadRun(bench, wl, headline=True, oracle_threads=threads)
+    rec = run.summary(args.steps, args.warmup)
+    ms_per_step = rec["step_us"] / 1e3
+    log(f"{wl.name}: step {rec['step_us']} us evicted median ({rec['GB_per_s']} GB/s, {rec['hbm_frac']:.1%} of peak), "
+        f"{rec['step_us_back_to_back']} us back to back")
+    kernels = rec["kernels"]
+    graph_us = None if args.no_graph else graph_replay(run, args.steps)
+    comparison = None
+    if not args.no_comparison and run.n_sel and wl.layers >= 3:
+        comparison = comparison_schedules(run, args.steps, rec["step_us_back_to_back"])
         log("comparison: " + ", ".join(f"{kk} {vv['step_us']} us" for kk, vv in comparison.items()))
-
-    # 6. Multi-token decode (last: it writes cache rows): T tokens, each appending its K/V rows and then
-    # running the step, each batch row starting T rows short of its length so that every token has room.
-    multi = None
-    if not args.no_multi_token:
-        T = args.steps
-        lens_mt = torch.clamp(lens - T, min=0).to(torch.int32)
-        kn = torch.randn((wl.layers, wl.batch, wl.kv_heads, wl.head_dim), device=dev).to(k.dtype)
-        vn = torch.randn_like(kn)
-
-        def token():
-            ppsa.append_kv(kn, vn, k, v, lens_mt)
-            ppsa.decode_step(sched, q, k, v, lens_mt, wl.topk, out=out, idx=idx, workspace=ws, sched_codes=codes)
-
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(T):
-            token()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ok = bool(torch.equal(lens_mt, torch.clamp(lens - T, min=0).to(torch.int32) + T))
-        multi = {"tokens": T, "us_per_token": round(e0.elapsed_time(e1) * 1e3 / T, 1),
-                 "start_lengths": "each batch row T rows short of its length", "lengths_grew_by_tokens": ok}
-        log(f"multi-token decode: {multi['us_per_token']} us per token (append + step)")
+    multi = None if args.no_multi_token else multi_token(run, args.steps)
+    cpu = None if run.timer is None else run.timer.result(run.step_bytes)
 
     # Roofline of the attention kernel with the largest share of the step.
-    attn_keys = [kk for kk in layer_bytes if kk in kernels]
+    attn_keys = [kk for kk in run.layer_bytes if kk in kernels]
     dom = max(attn_keys, key=lambda kk: kernels[kk]["us_per_step"])
     traffic, traffic_src = measured_traffic(wl.name, dom)
-    roofline = {"bound": "hbm", "kernel": f"{dom}: {ppsa.timing_kernel_name(ppsa.KERNEL_KEYS.index(dom))}",
+    achievable = None if probes is None else probes["read_4GiB_nontemporal"]["GB_per_s"]
+    roofline = {"bound": "hbm", "kernel": f"{dom}: {bench.ppsa.timing_kernel_name(bench.ppsa.KERNEL_KEYS.index(dom))}",
                 "achieved": kernels[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kernels[dom]["hbm_frac"], "traffic": traffic, "traffic_source": traffic_src,
-                "bytes_per_launch": layer_bytes[dom], "us_per_launch": kernels[dom]["us_per_launch"],
+                "achievable": achievable,
+                "frac_of_achievable": None if achievable is None else round(kernels[dom]["GB_per_s"] / achievable, 4),
+                "bytes_per_launch": run.layer_bytes[dom], "us_per_launch": kernels[dom]["us_per_launch"],
                 "launches_per_step": kernels[dom]["launches_per_step"]}
+    layer_key = {"attn_sparse": "sparse_layer", "attn_full": "full_layer"}.get(dom)
+    if layer_key and layer_key in rec["layers_timed"]:
+        roofline["with_merge_launch"] = rec["layers_timed"][layer_key]
+    run.free()
+    del run
 
-    sel_us = kernels.get("select", {}).get("us_per_step", 0.0)
-    if "attn_full_scores" in kernels and "attn_full" in kernels:
-        sel_us += n_sel * (kernels["attn_full_scores"]["us_per_launch"] - kernels["attn_full"]["us_per_launch"])
+    # The other workloads, timed the same way (no comparison schedules; oracle baselines on one thread for
+    # the two small ones, as the baseline plan asks).
+    others = {}
+    names = [] if args.workloads == "none" else (
+        [n for n in synth.WORKLOADS if n != wl.name] if args.workloads == "all" else args.workloads.split(","))
+    for name in names:
+        other = synth.WORKLOADS[name]
+        r = WorkloadRun(bench, other, headline=False, oracle_threads=0)
+        o = r.summary(args.steps, min(args.warmup, 2))
+        log(f"{name}: step {o['step_us']} us evicted median ({o['GB_per_s']} GB/s, {o['hbm_frac']:.1%}), "
+            f"{o['step_us_back_to_back']} us back to back; parity ok={None if o['parity'] is None else o['parity']['ok']}")
+        r.free()
+        del r
+        if not args.no_cpu_baseline and name in ("tiny-f32", "llama2-7b-10k"):
+            o["cpu_baseline_one_thread"] = one_thread_oracle(other)
+        others[name] = o
 
     copy_probe = None
     if args.copy_probe:
+        torch = bench.torch
         n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src = torch.empty(n, dtype=torch.uint8, device=bench.dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        for _ in range(10):
-            dst.copy_(src)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 10
+        us = bench.time_loop(lambda i: dst.copy_(src), 10)
         copy_probe = {"bytes_read": n, "bytes_written": n, "us": round(us, 1),
                       "GB_per_s_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}
         del src, dst
 
-    cpu = None if timer is None else timer.result(step_bytes)
-
     result = {
         "metric": METRIC,
-        "value": round(gbs, 1),
+        "value": rec["GB_per_s"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -414,19 +742,26 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch, "q_heads": wl.q_heads,
                    "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "seq_len": wl.max_len, "topk": wl.topk,
                    "select_layers": list(wl.select_layers), "parallelism": "single GPU"},
-        "step_us": round(ms_per_step * 1e3, 1),
-        "kv_bytes_per_step": step_bytes,
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "step_us_evicted": {"median": round(percentile(per_step, 50), 1), "p10": round(percentile(per_step, 10), 1),
-                            "p90": round(percentile(per_step, 90), 1)},
+        "timing": "value and ms_per_step: median of the steps, each timed after a 1 GiB cache-evicting write; "
+                  "step_us_back_to_back: the same steps without eviction",
+        "step_us": rec["step_us"],
+        "step_us_evicted": rec["step_us_evicted"],
+        "step_us_back_to_back": rec["step_us_back_to_back"],
         "step_us_graph_replay": graph_us,
-        "step_us_with_launch_timing": round(instrumented_us, 1),
-        "selection_overhead_frac": round(sel_us / (ms_per_step * 1e3), 4),
-        "comparison_schedules": comparison or None,
-        "multi_token_decode": multi,
+        "step_us_with_launch_timing": rec["step_us_with_launch_timing"],
+        "kv_bytes_per_step": rec["kv_bytes_per_step"],
+        "hbm_frac": rec["hbm_frac"],
+        "selection_overhead_frac": rec["selection_overhead_frac"],
         "kernels": kernels,
+        "layers_timed": rec["layers_timed"],
+        "gather_twin": rec.get("gather_twin"),
+        "parity": rec["parity"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "probes": probes,
+        "comparison_schedules": comparison,
+        "multi_token_decode": multi,
+        "workloads": others or None,
     }
     if copy_probe:
         result["copy_probe"] = copy_probe

@@ -274,6 +274,35 @@ int ppsa_timing_read(int32_t* counts, double* total_ms, int32_t num_kinds, int64
 /* Static description of a kernel kind ("unknown" outside the enum). */
 const char* ppsa_timing_kernel_name(int32_t kind);
 
+/*
+ * Measurement probes (instrumentation; not part of the method, never called
+ * by the entry points above). Each enqueues one kernel on `stream` and
+ * returns without waiting; time them with events on that stream. `sink` is a
+ * device int32 the kernels may write (so that no load is optimised away).
+ * Errors: PPSA_ERR_INVALID_ARG for bad arguments (before any HIP call),
+ * PPSA_ERR_HIP for a failed launch.
+ *
+ * ppsa_probe_read: reads `bytes` of device memory at `buf` once (16-byte
+ *   loads, each workgroup one contiguous chunk of 32 to 512 KiB, at least
+ *   2048 workgroups when the size allows); bytes must be a positive multiple
+ *   of 32 KiB and buf 16-byte aligned. nontemporal != 0
+ *   loads with the nontemporal hint, as the streaming attention launches do.
+ *   bytes / time is the achievable HBM read bandwidth when buf is much larger
+ *   than the last-level cache (256 MB).
+ * ppsa_probe_empty: an empty kernel of `groups` workgroups of `threads`
+ *   (1..1024) work-items; back-to-back launches give the per-launch floor.
+ * ppsa_probe_gather: `repeats` (>= 1) back-to-back launches of the load-only
+ *   twin of ppsa_sparse_attn's kernel for these dims and idx (same plan,
+ *   grid, waves, slot-entry reads and K/V row loads; no attention arithmetic,
+ *   no merge, no output). The sparse kernel's time over the twin's is what
+ *   its arithmetic, LDS traffic and epilogue cost on top of the gather. bf16,
+ *   head_dim 128 only (the matrix-core path), else PPSA_ERR_UNSUPPORTED.
+ */
+int ppsa_probe_read(const void* buf, size_t bytes, int32_t nontemporal, int32_t* sink, void* stream);
+int ppsa_probe_empty(int32_t groups, int32_t threads, int32_t* sink, void* stream);
+int ppsa_probe_gather(const ppsa_dims* dims, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                      const int32_t* idx, int32_t topk, int32_t repeats, int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

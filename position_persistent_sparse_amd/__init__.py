@@ -66,13 +66,17 @@ def _load():
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
     lib.ppsa_decode_step_static.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.ppsa_probe_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.ppsa_probe_empty.argtypes = [i32, i32, vp, vp]
+    lib.ppsa_probe_gather.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp]
     lib.ppsa_timing_enable.argtypes = [i32]
     lib.ppsa_timing_read.argtypes = [vp, vp, i32, vp]
     lib.ppsa_timing_kernel_name.argtypes = [i32]
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
                  "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read",
-                 "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static"):
+                 "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static", "ppsa_probe_read",
+                 "ppsa_probe_empty", "ppsa_probe_gather"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -311,6 +315,27 @@ def timing_read() -> dict:
 
 def timing_kernel_name(kind: int) -> str:
     return _lib.ppsa_timing_kernel_name(int(kind)).decode()
+
+
+def probe_read(buf, nontemporal: bool, sink):
+    """Measurement probe: one read of the whole byte buffer `buf` (a multiple of 32 KiB)."""
+    _check(_lib.ppsa_probe_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)), _ptr(sink),
+                                _stream(buf.device)), "ppsa_probe_read")
+
+
+def probe_empty(groups: int, threads: int, sink):
+    """Measurement probe: one empty kernel launch."""
+    _check(_lib.ppsa_probe_empty(int(groups), int(threads), _ptr(sink), _stream(sink.device)), "ppsa_probe_empty")
+
+
+def probe_gather(k_cache, v_cache, seq_lens, idx, q_heads: int, sink, repeats: int = 1, scale: float = 0.0):
+    """Measurement probe: `repeats` back-to-back launches of the load-only twin of sparse_attn's kernel over
+    K/V [B,Hkv,N,d] and idx [B,Hkv,k]."""
+    B, Hkv, N, d = k_cache.shape
+    dims = make_dims(B, q_heads, Hkv, d, N, k_cache.dtype, scale)
+    _check(_lib.ppsa_probe_gather(ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(idx),
+                                  int(idx.shape[-1]), int(repeats), _ptr(sink), _stream(k_cache.device)),
+           "ppsa_probe_gather")
 
 
 def raw_library():

@@ -25,6 +25,7 @@
 #include "attn_epilogue.h"
 #include "device_common.h"
 #include "mfma_tile.h"
+#include "sparse_gather.h"
 #include "ppsa_internal.h"
 #include "ppsa.h"
 
@@ -33,64 +34,19 @@ namespace {
 
 using namespace mt;
 
-typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 4;          // multi-split launches: two workgroups per CU
 constexpr int kWavesSingle = 8;    // one split per unit: one long workgroup per unit
 constexpr int kORow = kD + 4;      // floats per head row of a wave's partial output in LDS (bank spread)
 constexpr int kMaxRowsPerSplit = 1 << 20;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9 data format
 
 __host__ __device__ constexpr int wave_floats(int group) {
   return kKBlockBytes / 4 > group * kORow ? kKBlockBytes / 4 : group * kORow;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
 __device__ __forceinline__ void store_out4(uint16_t* p, float4_t o, float inv) {
   const uint32_t lo = (uint32_t)bf16_round(o[0] * inv) | ((uint32_t)bf16_round(o[1] * inv) << 16);
   const uint32_t hi = (uint32_t)bf16_round(o[2] * inv) | ((uint32_t)bf16_round(o[3] * inv) << 16);
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
-}
-
-// Raw slot entries of the tile's rows 16 blk + 4g + i (i = 0..3), `rel` = the tile's first slot
-// relative to the split, through a buffer resource over the split's slots: reads past the split
-// return 0 (the slot index marks them invalid at use). Unconditional loads: nothing waits on them
-// until the rows are requested.
-__device__ __forceinline__ void fetch_positions(int (&raw)[2][4], __amdgpu_buffer_rsrc_t r, int rel, bool vec, int g) {
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const uint32_t off = (uint32_t)(rel + 16 * blk + 4 * g) * 4u;
-    if (vec) {
-      const u32x4v_t w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[blk][i] = (int)w[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[blk][i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, off + 4u * i, 0, 0);
-    }
-  }
-}
-
-// Lane (g, n) loads bytes 16n .. 16n+15 of the rows of slots rel + 16 blk + 4g + i of K and V. A
-// slot past the split or an entry outside [0, n_live) loads row 0 and stays invalid.
-template <bool STREAM>
-__device__ __forceinline__ void load_gathered(Tile& t, const char* kb, const char* vb, const int (&raw)[2][4], int rel,
-                                              int nrows, int n_live, int g, int n) {
-  t.valid = 0u;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = raw[blk][i];
-      const bool ok = rel + 16 * blk + 4 * g + i < nrows && (uint32_t)p < (uint32_t)n_live;
-      const uint32_t off = (uint32_t)(ok ? p : 0) * kRowBytes + 16u * n;
-      t.valid |= (uint32_t)ok << (4 * blk + i);
-      t.k[blk][i] = load16<STREAM>(kb, off);
-      t.v[blk][i] = load16<STREAM>(vb, off);
-    }
 }
 
 template <int WAVES, bool STREAM>
@@ -217,16 +173,24 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+int attn_sparse_waves(const AttnArgs& a) {
+  // One split per unit means one workgroup per unit: twice the waves keep more rows in flight per
+  // CU while the LDS stays within 64 KiB.
+  return a.splits == 1 && (size_t)kWavesSingle * wave_floats(a.group) * sizeof(float) <= 65536 ? kWavesSingle
+                                                                                               : kWaves;
+}
+
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t stream) {
   if (a.splits <= 0 || a.batch <= 0 || a.kv_heads <= 0) return hipSuccess;
   if (a.group < 1 || a.group > kMaxGroup || a.rows_per_split <= 0 || a.rows_per_split > kMaxRowsPerSplit)
     return hipErrorInvalidValue;
   if ((int64_t)a.splits * a.rows_per_split < a.kslots) return hipErrorInvalidValue;
   if ((int64_t)a.batch * a.kv_heads * a.splits > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.splits == 1) {
-    if ((size_t)kWavesSingle * wave_floats(a.group) * sizeof(float) <= 65536) return launch_cfg<kWavesSingle, false>(a, stream);
-    return launch_cfg<kWaves, false>(a, stream);
-  }
+  // Several splits per unit stream (nontemporal loads: bandwidth-bound); one split is bound by
+  // latency and loads plainly.
+  if (a.splits == 1)
+    return attn_sparse_waves(a) == kWavesSingle ? launch_cfg<kWavesSingle, false>(a, stream)
+                                                : launch_cfg<kWaves, false>(a, stream);
   return launch_cfg<kWaves, true>(a, stream);
 }
 

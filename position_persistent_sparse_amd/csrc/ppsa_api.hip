@@ -435,6 +435,54 @@ int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new,
   return finish(timed(KERNEL_APPEND, st, [&] { return launch_append(a, st); }));
 }
 
+int ppsa_probe_read(const void* buf, size_t bytes, int32_t nontemporal, int32_t* sink, void* stream) {
+  constexpr size_t kUnit = (size_t)32 << 10;
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes == 0 || bytes % kUnit != 0 ||
+      bytes / kUnit > 0x7fffffff)
+    return PPSA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(launch_read_probe(buf, bytes, nontemporal != 0, sink, static_cast<hipStream_t>(stream)));
+}
+
+int ppsa_probe_empty(int32_t groups, int32_t threads, int32_t* sink, void* stream) {
+  if (groups < 1 || threads < 1 || threads > 1024 || !sink || !aligned(sink, 4)) return PPSA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return finish(launch_empty_probe(groups, threads, sink, static_cast<hipStream_t>(stream)));
+}
+
+int ppsa_probe_gather(const ppsa_dims* dims, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                      const int32_t* idx, int32_t topk, int32_t repeats, int32_t* sink, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != PPSA_OK) return rc;
+  if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
+  if (repeats < 1) return PPSA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return PPSA_OK;
+  if (!k_cache || !v_cache || !seq_lens || !idx || !sink || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(seq_lens, 4) || !aligned(idx, 4) || !aligned(sink, 4))
+    return PPSA_ERR_INVALID_ARG;
+  Ctx c{dims, make_plan(*dims, topk), nullptr, static_cast<hipStream_t>(stream)};
+  if (!c.plan.mfma) return PPSA_ERR_UNSUPPORTED;  // the twin mirrors the matrix-core sparse launch
+  if (!c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.idx = idx;
+  a.batch = dims->batch;
+  a.q_heads = dims->num_q_heads;
+  a.kv_heads = dims->num_kv_heads;
+  a.group = dims->num_q_heads / dims->num_kv_heads;
+  a.max_len = dims->max_seq_len;
+  a.kslots = topk;
+  a.splits = c.plan.sparse_splits;
+  a.rows_per_split = c.plan.sparse_rows;
+  a.idx_vec = (topk % 4 == 0 && aligned(idx, 16)) ? 1 : 0;
+  (void)hipGetLastError();
+  for (int r = 0; r < repeats; ++r)
+    if ((rc = finish(launch_gather_twin(a, sink, c.stream))) != PPSA_OK) return rc;
+  return PPSA_OK;
+}
+
 int ppsa_decode_step(const ppsa_dims* dims, int32_t num_layers, const int32_t* schedule, const void* q,
                      const void* k_cache, const void* v_cache, const int32_t* seq_lens, int32_t topk, void* out,
                      int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {

@@ -101,6 +101,14 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int mode, hipStream_t stream);
 // Sparse layer on the matrix cores (attn_sparse.hip, same contract as MODE_SPARSE): partials for
 // launch_combine, or the output itself when the unit has one split.
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t stream);
+// Waves per workgroup of that launch.
+int attn_sparse_waves(const AttnArgs& a);
+
+// Measurement probes (probe.hip; instrumentation, not the method): a plain read of `bytes` (a
+// multiple of 32 KiB), an empty kernel, and the sparse launch's load-only twin.
+hipError_t launch_read_probe(const void* buf, size_t bytes, bool nontemporal, int32_t* sink, hipStream_t stream);
+hipError_t launch_empty_probe(int groups, int threads, int32_t* sink, hipStream_t stream);
+hipError_t launch_gather_twin(const AttnArgs& a, int32_t* sink, hipStream_t stream);
 // Largest group size the attention kernels take.
 constexpr int kMaxGroup = 16;
 // Most splits one unit may be cut into (the merge pass keeps one weight per split in LDS).

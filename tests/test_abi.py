@@ -223,3 +223,20 @@ def test_static_scratch_step_validation():
     big = dims(batch=8, q_heads=64, kv_heads=8, max_seq_len=300000)
     assert static_step(big, "FFXS") == ppsa.PPSA_ERR_SCRATCH
     assert ppsa.status_string(ppsa.PPSA_ERR_SCRATCH) != "unknown status"
+
+
+def test_probe_validation():
+    """The measurement probes check their arguments before any HIP call."""
+    assert LIB.ppsa_probe_read(None, 1 << 20, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_read(FAKE, (1 << 20) + 16, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG  # not 32 KiB units
+    assert LIB.ppsa_probe_read(ODD, 1 << 20, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_read(FAKE, 0, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_empty(0, 64, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_empty(4, 2048, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_empty(4, 64, None, None) == ppsa.PPSA_ERR_INVALID_ARG
+    d = dims()
+    assert LIB.ppsa_probe_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 16, 0, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    assert LIB.ppsa_probe_gather(ctypes.byref(d), None, FAKE, FAKE, FAKE, 16, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
+    f32 = dims(dtype=ppsa.PPSA_F32, head_dim=64)
+    assert LIB.ppsa_probe_gather(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, None) == ppsa.PPSA_ERR_UNSUPPORTED
