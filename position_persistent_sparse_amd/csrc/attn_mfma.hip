@@ -139,8 +139,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   }
 
   // Wave result: head n's max and normaliser; O rows are heads 4g + j, dims 8n + t.
-  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_rows4(st.l_run);
   if (g == 0 && n < group) {
     sm_m[wave][n] = st.m_run;
     sm_l[wave][n] = l_tot;

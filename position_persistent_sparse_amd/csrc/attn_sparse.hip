@@ -44,9 +44,7 @@ __host__ __device__ constexpr int wave_floats(int group) {
 }
 
 __device__ __forceinline__ void store_out4(uint16_t* p, float4_t o, float inv) {
-  const uint32_t lo = (uint32_t)bf16_round(o[0] * inv) | ((uint32_t)bf16_round(o[1] * inv) << 16);
-  const uint32_t hi = (uint32_t)bf16_round(o[2] * inv) | ((uint32_t)bf16_round(o[3] * inv) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(p) = make_uint2(bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv));
 }
 
 template <int WAVES, bool STREAM>
@@ -114,8 +112,7 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 
   // Wave result to LDS: head n's max and normaliser; O rows (heads 4g + j, dims 8n + t) as two
   // 16-byte pieces per head, rows padded to kORow floats.
-  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_rows4(st.l_run);
   if (g == 0 && n < group) {
     sm_m[wave][n] = st.m_run;
     sm_l[wave][n] = l_tot;

@@ -15,8 +15,8 @@
 //       B = V needs rows along the operand elements: lane (g, n) holds rows 4g..4g+3 at dims
 //       8n..8n+7 (16 lanes cover a whole 256-byte row) and product t uses dim 8n+t of each,
 //       regrouped with v_perm_b32. The output column n of product t is dim 8n+t.
-// The running max is shared by the four lanes holding a head (two xor shuffles per tile) and only
-// moved when a tile exceeds it by more than 2^8 ("lazy" rescaling: weights may reach 256, still
+// The running max is shared by the four lanes holding a head (a max across the wave's four rows
+// per tile) and only moved when a tile exceeds it by more than 2^8 ("lazy" rescaling: weights may reach 256, still
 // exact in the float32 sums); a merge uses each partial's own max, so the result is the same
 // softmax. Weights are rounded to bf16 for the product and the normaliser sums the rounded
 // weights, so numerator and denominator match.
@@ -33,6 +33,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;
@@ -58,8 +60,26 @@ struct Online {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two floats to two bf16 (low half first), round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  return (uint32_t)bf16_round(lo) | ((uint32_t)bf16_round(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
+// Max and sum over the four lanes n, n+16, n+32, n+48 (the four 16-lane rows of a wave), every lane
+// getting the result: v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two halves (VALU
+// instructions; no trip through the LDS crossbar). Each sum adds the lower row to the upper one, so
+// all four lanes hold the bit-identical value.
+__device__ __forceinline__ float max_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& u, int w) {
@@ -136,19 +156,20 @@ __device__ __forceinline__ void softmax_pv(const Tile& t, const float (&x)[2][4]
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, x[blk][j]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_rows4(tmax);
   const bool need = tmax > st.m_run + kLazyLog2;
   if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
     const float m_new = need ? fmaxf(st.m_run, tmax) : st.m_run;
-    const float alpha = m_new == st.m_run ? 1.0f : exp2_fast(st.m_run - m_new);
-    st.l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(st.m_run != -INFINITY) != 0ull) {
+      const float alpha = m_new == st.m_run ? 1.0f : exp2_fast(st.m_run - m_new);
+      st.l_run *= alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float aj = __shfl(alpha, 4 * g + j);  // lane 4g+j holds head 4g+j
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * g + j);  // lane 4g+j holds head 4g+j
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) st.acc[tt][j] *= aj;
-    }
+        for (int tt = 0; tt < 8; ++tt) st.acc[tt][j] *= aj;
+      }
+    }  // else nothing is accumulated yet (every sum is still zero): no rescaling to do
     st.m_run = m_new;
   }
   const float ms = st.m_run == -INFINITY ? 0.0f : st.m_run;
