@@ -275,6 +275,18 @@ int ppsa_timing_read(int32_t* counts, double* total_ms, int32_t num_kinds, int64
 const char* ppsa_timing_kernel_name(int32_t kind);
 
 /*
+ * Split-planner override (tuning and testing; not part of the method). Each
+ * attention layer is cut into splits of rows per (batch row, KV head), merged
+ * afterwards; the library sizes them for this GPU. full_rows / sparse_rows > 0
+ * set the rows of one split of full / sparse layers (rounded up to the
+ * kernels' granule, capped as the automatic plan is); 0 restores the
+ * automatic choice. Process-wide; affects ppsa_workspace_bytes and every
+ * later call. Results do not depend on the plan beyond float32 rounding.
+ * Returns PPSA_OK, or PPSA_ERR_INVALID_ARG for a negative value.
+ */
+int ppsa_set_split_rows(int32_t full_rows, int32_t sparse_rows);
+
+/*
  * Measurement probes (instrumentation; not part of the method, never called
  * by the entry points above). Each enqueues one kernel on `stream` and
  * returns without waiting; time them with events on that stream. `sink` is a

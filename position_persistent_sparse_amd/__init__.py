@@ -66,6 +66,7 @@ def _load():
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
     lib.ppsa_decode_step_static.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.ppsa_set_split_rows.argtypes = [i32, i32]
     lib.ppsa_probe_read.argtypes = [vp, sz, i32, vp, vp]
     lib.ppsa_probe_empty.argtypes = [i32, i32, vp, vp]
     lib.ppsa_probe_gather.argtypes = [dp, vp, vp, vp, vp, i32, i32, vp, vp]
@@ -75,7 +76,8 @@ def _load():
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
                  "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read",
-                 "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static", "ppsa_probe_read",
+                 "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static", "ppsa_set_split_rows",
+                 "ppsa_probe_read",
                  "ppsa_probe_empty", "ppsa_probe_gather"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -315,6 +317,11 @@ def timing_read() -> dict:
 
 def timing_kernel_name(kind: int) -> str:
     return _lib.ppsa_timing_kernel_name(int(kind)).decode()
+
+
+def set_split_rows(full_rows: int = 0, sparse_rows: int = 0):
+    """Planner override (process-wide): rows per split of full and sparse layers; 0 = automatic."""
+    _check(_lib.ppsa_set_split_rows(int(full_rows), int(sparse_rows)), "ppsa_set_split_rows")
 
 
 def probe_read(buf, nontemporal: bool, sink):

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "ppsa_internal.h"
@@ -48,6 +49,10 @@ bool use_mfma(const ppsa_dims& d) {
   const bool offsets_fit = (int64_t)d.max_seq_len * d.head_dim * 2 < (int64_t(1) << 32);
   return !force_valu && offsets_fit && attn_mfma_supported(d.dtype, d.head_dim, d.num_q_heads / d.num_kv_heads);
 }
+
+// Planner override (ppsa_set_split_rows): rows per split of full and sparse layers, 0 = automatic.
+std::atomic<int> g_full_rows_override{0};
+std::atomic<int> g_sparse_rows_override{0};
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -93,6 +98,7 @@ Plan make_plan(const ppsa_dims& d, int topk, bool variants = true, bool score_bu
   int64_t rows = ceil_div(units * d.max_seq_len, kFullTargetGroups);
   rows = std::max<int64_t>(rows, ceil_div(d.max_seq_len, kMaxSplitsPerUnit));
   if ((int64_t)d.max_seq_len * kv_row_bytes <= kSingleSplitBytes) rows = d.max_seq_len;
+  if (const int o = g_full_rows_override.load(std::memory_order_relaxed)) rows = std::max<int64_t>(o, ceil_div(d.max_seq_len, kMaxSplitsPerUnit));
   p.full_rows = std::max(round_up(rows, granule), granule);
   if (p.mfma) p.full_rows = std::min(p.full_rows, attn_mfma_max_score_rows(d.num_q_heads / d.num_kv_heads));
   p.full_splits = (int)ceil_div(d.max_seq_len, p.full_rows);
@@ -101,6 +107,7 @@ Plan make_plan(const ppsa_dims& d, int topk, bool variants = true, bool score_bu
     rows = ceil_div(units * topk, kSparseTargetGroups);
     rows = std::max<int64_t>(rows, ceil_div(topk, kMaxSplitsPerUnit));
     if ((int64_t)topk * kv_row_bytes <= kSingleSplitBytes) rows = topk;
+    if (const int o = g_sparse_rows_override.load(std::memory_order_relaxed)) rows = std::max<int64_t>(o, ceil_div(topk, kMaxSplitsPerUnit));
     const int cap = p.mfma ? (1 << 20) : attn_max_sparse_rows() / granule * granule;
     p.sparse_rows = std::max(round_up(rows, granule), granule);
     if (p.sparse_rows > cap) {
@@ -433,6 +440,13 @@ int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new,
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   return finish(timed(KERNEL_APPEND, st, [&] { return launch_append(a, st); }));
+}
+
+int ppsa_set_split_rows(int32_t full_rows, int32_t sparse_rows) {
+  if (full_rows < 0 || sparse_rows < 0) return PPSA_ERR_INVALID_ARG;
+  g_full_rows_override.store(full_rows, std::memory_order_relaxed);
+  g_sparse_rows_override.store(sparse_rows, std::memory_order_relaxed);
+  return PPSA_OK;
 }
 
 int ppsa_probe_read(const void* buf, size_t bytes, int32_t nontemporal, int32_t* sink, void* stream) {

@@ -7,6 +7,10 @@ import oracle
 from oracle import compare
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+# Relative L2 error of a bf16 layer output: the output rounding alone is at most half a bf16 spacing
+# (2^-9 relative) per element, the weight rounding adds about as much again at most, so a layer's
+# error vector stays under 2^-8 of the reference's norm; a precision regression would not.
+REL_L2_BF16 = 2.0 ** -8
 
 
 def bf16_ulp(x):
@@ -30,6 +34,10 @@ def check_output(got, want, dtype, where, abs_weighted=None):
     assert np.all(np.isfinite(got)), f"{where}: non-finite output"
     worst = float(err.max()) if err.size else 0.0
     assert worst <= TOL[dtype], f"{where}: max abs error {worst:.3e} > {TOL[dtype]}"
+    ref_norm = float(np.linalg.norm(want))
+    if dtype == "bf16" and ref_norm > 0.0:
+        rel = float(np.linalg.norm(got - want)) / ref_norm
+        assert rel <= REL_L2_BF16, f"{where}: relative L2 error {rel:.3e} > 2^-8"
     if dtype == "bf16" and abs_weighted is not None:
         bound = 2.0 ** -7 * 1.01 * abs_weighted + bf16_ulp(want) + 1e-5
         bad = int(np.sum(err > bound))

@@ -240,3 +240,15 @@ def test_probe_validation():
     assert LIB.ppsa_probe_gather(ctypes.byref(d), None, FAKE, FAKE, FAKE, 16, 1, FAKE, None) == ppsa.PPSA_ERR_INVALID_ARG
     f32 = dims(dtype=ppsa.PPSA_F32, head_dim=64)
     assert LIB.ppsa_probe_gather(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, None) == ppsa.PPSA_ERR_UNSUPPORTED
+
+
+def test_split_rows_override_changes_the_plan():
+    d = dims(batch=4, q_heads=32, kv_heads=8, max_seq_len=32768)
+    auto = ppsa.workspace_bytes(d, 4096)
+    try:
+        assert LIB.ppsa_set_split_rows(-1, 0) == ppsa.PPSA_ERR_INVALID_ARG
+        ppsa.set_split_rows(128, 128)  # many more splits: larger partial regions
+        assert ppsa.workspace_bytes(d, 4096) > auto
+    finally:
+        ppsa.set_split_rows(0, 0)
+    assert ppsa.workspace_bytes(d, 4096) == auto

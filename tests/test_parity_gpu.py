@@ -479,3 +479,42 @@ def test_decode_step_coverage_budget(name, tau, cap):
                 assert ok, f"coverage {name} layer {layer} b={b} h={h}: {msg}"
                 assert compare.check_selection_exact(row, sc_h[sel, b, h], n, k_gpu), (layer, b, h)
     say(f"[parity] coverage {name} tau={tau}: ok, kept per unit {min(kept)}..{max(kept)}")
+
+
+def test_results_do_not_depend_on_the_split_plan():
+    """One reduced LLaMA-3-8B-shaped step (group 4, several selection and sparse layers) under three split
+    plans -- automatic, many small splits, and one split per (batch row, KV head) -- through the planner
+    override: identical selections, and outputs that differ by at most the rounding the plans may
+    legitimately change (the weights' bf16 rounding, relative to each split's own running max, moves an
+    output by at most 2^-7 of the attention of |V|, and the output's own rounding by one bf16 spacing)."""
+    wl = REDUCED["llama3-8b-gqa-32k"].with_(layers=6, select_layers=(2, 4))
+    gen = synth.Generator(wl)
+    say(f"[splits] L={wl.layers} B={wl.batch} Hq={wl.q_heads} Hkv={wl.kv_heads} N={wl.max_len} k={wl.topk}")
+    q, k, v, lens, host = torch_io.upload(wl, gen, DEV)
+    results = {}
+    plans = {"automatic": (0, 0), "small splits": (128, 128), "one split": (wl.max_len, wl.topk)}
+    try:
+        for name, (fr, sr) in plans.items():
+            ppsa.set_split_rows(fr, sr)
+            out, idx = ppsa.decode_step(wl.schedule(), q, k, v, lens, wl.topk)
+            torch.cuda.synchronize()
+            results[name] = (widen_out(torch_io.from_torch(out), wl), idx.cpu().numpy())
+    finally:
+        ppsa.set_split_rows(0, 0)
+    scale = oracle.default_scale(wl.head_dim)
+    ref_out, ref_idx = results["automatic"]
+    sel = -1
+    for layer, kind in enumerate(wl.schedule()):
+        if kind == "X":
+            sel += 1
+        qh, kh, vh = host[layer]
+        selection = ref_idx[sel] if kind == "S" else None
+        absw, _, _ = oracle.decode_layer(kind, qh, kh, np.asarray(vh) & np.uint16(0x7FFF), gen.seq_lens, wl.group,
+                                         wl.topk, scale, wl.dtype, selection)
+        for name, (o, i) in results.items():
+            assert np.array_equal(i, ref_idx), f"{name}: selections differ"
+            diff = np.abs(o[layer] - ref_out[layer])
+            bound = 2 * (2.0 ** -7 * 1.01 * absw) + 2 * (2.0 ** -8) * np.abs(ref_out[layer]) + 2e-5
+            bad = int(np.sum(diff > bound))
+            assert bad == 0, f"{name} layer {layer} ({kind}): {bad} elements differ beyond the rounding bound"
+    say("[splits] ok: three plans agree")
