@@ -227,13 +227,18 @@ int ppsa_decode_step_static(const ppsa_dims* dims, int32_t num_layers, const int
  *   k_new, v_new:  [L, B, Hkv, d], element type `dtype`
  *   k/v_cache:     [L, B, Hkv, Nmax, d], written at one row per (l, b, h)
  *   seq_lens:      [B] int32, read and written on the device
- * One kernel on `stream`: a ppsa_decode_step enqueued after it on the same
- * stream sees the new rows and lengths. A multi-token decode calls this,
- * then ppsa_decode_step, once per token. Pointers must be 16-byte aligned
- * (seq_lens 4-byte); errors as for the other entry points.
+ *   overflow:      device int32 or NULL; when given, the number of batch rows
+ *                  that were full (whose token was not stored) is added to it,
+ *                  so a caller running past the cache's capacity can see it
+ * Two launches on `stream`, in order: the row copy, then the length update
+ * (which reads and counts the lengths the copy used). A ppsa_decode_step
+ * enqueued after them on the same stream sees the new rows and lengths. A
+ * multi-token decode calls this, then ppsa_decode_step, once per token.
+ * Pointers must be 16-byte aligned (seq_lens and overflow 4-byte); errors as
+ * for the other entry points.
  */
 int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new, const void* v_new,
-                   void* k_cache, void* v_cache, int32_t* seq_lens, void* stream);
+                   void* k_cache, void* v_cache, int32_t* seq_lens, int32_t* overflow, void* stream);
 
 /*
  * Launch timing (instrumentation; not part of the method). While timing is

@@ -64,7 +64,7 @@ def _load():
                                         vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
-    lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp]
+    lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ppsa_decode_step_static.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     lib.ppsa_set_split_rows.argtypes = [i32, i32]
     lib.ppsa_probe_read.argtypes = [vp, sz, i32, vp, vp]
@@ -281,9 +281,11 @@ def decode_step_static(schedule, q, k_cache, v_cache, seq_lens, topk: int, out=N
     return out, idx
 
 
-def append_kv(k_new, v_new, k_cache, v_cache, seq_lens):
+def append_kv(k_new, v_new, k_cache, v_cache, seq_lens, overflow=None):
     """Append one token: k_new/v_new [L,B,Hkv,d] go to row seq_lens[b] of the caches [L,B,Hkv,Nmax,d];
-    seq_lens (device int32) grows by one per batch row with room."""
+    seq_lens (device int32) grows by one per batch row with room. A full row (seq_lens[b] == Nmax) drops
+    its token: the caller must keep within capacity, and can pass `overflow` (a device int32 [1] tensor)
+    to which the number of dropped tokens is added."""
     _require(k_cache.dim() == 5 and v_cache.shape == k_cache.shape, "k_cache/v_cache must be [L,B,Hkv,Nmax,d]")
     L, B, Hkv, n_max, d = k_cache.shape
     for name, t in (("k_new", k_new), ("v_new", v_new)):
@@ -294,9 +296,12 @@ def append_kv(k_new, v_new, k_cache, v_cache, seq_lens):
              "caches must be contiguous with one dtype")
     _require(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,) and seq_lens.device == k_cache.device,
              "seq_lens must be int32 [B] on the cache's device")
+    if overflow is not None:
+        _require(overflow.dtype == torch.int32 and overflow.numel() >= 1 and overflow.device == k_cache.device,
+                 "overflow must be a device int32 tensor")
     dims = make_dims(B, Hkv, Hkv, d, n_max, k_cache.dtype)
     _check(_lib.ppsa_append_kv(ctypes.byref(dims), L, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                               _ptr(seq_lens), _stream(k_cache.device)), "ppsa_append_kv")
+                               _ptr(seq_lens), _ptr(overflow), _stream(k_cache.device)), "ppsa_append_kv")
 
 
 def timing_enable(capacity: int):

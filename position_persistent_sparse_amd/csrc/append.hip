@@ -8,7 +8,8 @@
 //     pieces (a layer's rows of one batch row are a few KiB, so the copy
 //     spreads over B x L workgroups rather than a few CUs);
 //  2. one workgroup stores the new lengths, after every copy has read the
-//     old ones (the kernel boundary orders the two).
+//     old ones (the kernel boundary orders the two), and adds the number of
+//     full batch rows to the caller's overflow counter when one is given.
 // A full row (n = Nmax) takes nothing.
 #include "device_common.h"
 #include "ppsa_internal.h"
@@ -39,7 +40,18 @@ __global__ __launch_bounds__(kThreads) void append_rows_kernel(AppendArgs a) {
 }
 
 __global__ __launch_bounds__(kThreads) void append_lengths_kernel(AppendArgs a) {
-  for (int b = threadIdx.x; b < a.batch; b += kThreads) a.seq_lens[b] = min(max(a.seq_lens[b], 0) + 1, a.max_len);
+  __shared__ int sm_full;
+  if (threadIdx.x == 0) sm_full = 0;
+  __syncthreads();
+  int full = 0;
+  for (int b = threadIdx.x; b < a.batch; b += kThreads) {
+    const int n = max(a.seq_lens[b], 0);
+    full += n >= a.max_len;
+    a.seq_lens[b] = min(n + 1, a.max_len);
+  }
+  if (full) atomicAdd(&sm_full, full);
+  __syncthreads();
+  if (threadIdx.x == 0 && a.overflow != nullptr && sm_full != 0) *a.overflow += sm_full;
 }
 
 }  // namespace

@@ -417,16 +417,17 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
 }
 
 int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new, const void* v_new,
-                   void* k_cache, void* v_cache, int32_t* seq_lens, void* stream) {
+                   void* k_cache, void* v_cache, int32_t* seq_lens, int32_t* overflow, void* stream) {
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if (num_layers < 0) return PPSA_ERR_INVALID_ARG;
   if (dims->batch == 0 || num_layers == 0) return PPSA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return PPSA_ERR_INVALID_ARG;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(seq_lens, 4))
+      !aligned(seq_lens, 4) || (overflow && !aligned(overflow, 4)))
     return PPSA_ERR_INVALID_ARG;
   AppendArgs a{};
+  a.overflow = overflow;
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_cache = k_cache;

@@ -122,6 +122,7 @@ struct AppendArgs {
   void* k_cache;
   void* v_cache;
   int32_t* seq_lens;
+  int32_t* overflow;        // or null: incremented by the number of full rows (tokens not stored)
   int32_t layers, batch, kv_heads, max_len, row_bytes;
 };
 

@@ -156,8 +156,8 @@ def test_timing_api_without_gpu_work():
     assert ppsa.timing_kernel_name(-1) == "unknown"
 
 
-def append(d, layers=2, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE):
-    return LIB.ppsa_append_kv(ctypes.byref(d), layers, kn, vn, kc, vc, lens, None)
+def append(d, layers=2, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, overflow=None):
+    return LIB.ppsa_append_kv(ctypes.byref(d), layers, kn, vn, kc, vc, lens, overflow, None)
 
 
 def test_append_kv_validation():
@@ -170,6 +170,7 @@ def test_append_kv_validation():
     for kw in ("kn", "vn", "kc", "vc"):
         assert append(d, **{kw: ODD}) == ppsa.PPSA_ERR_INVALID_ARG, kw
     assert append(d, lens=ctypes.c_void_p(0x100002)) == ppsa.PPSA_ERR_INVALID_ARG
+    assert append(d, overflow=ctypes.c_void_p(0x100002)) == ppsa.PPSA_ERR_INVALID_ARG
     assert append(dims(head_dim=96)) == ppsa.PPSA_ERR_UNSUPPORTED
     assert append(dims(batch=-1)) == ppsa.PPSA_ERR_INVALID_ARG
 

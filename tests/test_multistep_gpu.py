@@ -40,15 +40,20 @@ def test_append_kv_rows_and_lengths_exact(dtype, d):
     lens = torch.from_numpy(lens0.copy()).to(DEV)
     Kh, Vh = [K[layer].copy() for layer in range(L)], [V[layer].copy() for layer in range(L)]
     lens_h = lens0
+    overflow = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dropped = 0
     for step in range(2):
         kn, vn = storage(rng, (L, B, Hkv, d), dtype), storage(rng, (L, B, Hkv, d), dtype)
-        ppsa.append_kv(torch_io.to_torch(kn).to(DEV), torch_io.to_torch(vn).to(DEV), kt, vt, lens)
+        ppsa.append_kv(torch_io.to_torch(kn).to(DEV), torch_io.to_torch(vn).to(DEV), kt, vt, lens, overflow=overflow)
+        dropped += int(np.sum(np.clip(lens_h, 0, n_max) == n_max))  # rows already full drop this token
         lens_h = oracle.append_kv(Kh, Vh, lens_h, kn, vn)
         torch.cuda.synchronize()
         assert lens.cpu().numpy().tolist() == lens_h.tolist(), step
         np.testing.assert_array_equal(torch_io.from_torch(kt), np.stack(Kh))
         np.testing.assert_array_equal(torch_io.from_torch(vt), np.stack(Vh))
+        assert int(overflow.item()) == dropped, step
     assert lens_h.tolist() == [40, 40, 2, 19, 2]
+    assert dropped == 3  # the full row twice, the row with one slot of room on the second token
 
 
 def test_multi_token_decode_matches_oracle():
