@@ -5,18 +5,20 @@ selection, sparse) through the C ABI entry point ppsa_decode_step, with all
 inputs resident in HBM, and prints one JSON line.
 
 Headline (`value`, `ms_per_step`): the workload the metric is quoted on
-(LLaMA-3-8B GQA, 32K context), timed by the survey's protocol: K steps, each
-preceded (outside its HIP events) by a 1 GiB write that evicts the last-level
-cache and the L2s, reported as the median; `value` is the algorithmic K+V
+(LLaMA-3-8B GQA, 32K context): K steps, each preceded (outside its HIP
+events) by a 1 GiB read that evicts the last-level cache and the L2s,
+reported as the median; `value` is the algorithmic K+V
 bytes of one step over that median. The same K steps back to back without
 eviction are reported beside it (`step_us_back_to_back`).
 
 The line also carries: per-kernel durations from the library's launch timing
 (HIP events around each launch, on the launch stream) and per-layer figures
-(attention launch plus its merge launch); the roofline of the dominant kernel
+(attention launch plus its merge launch, and the two launches apart, each
+back to back in a captured graph); the roofline of the dominant kernel
 against the 8 TB/s peak and against the read bandwidth this GPU reaches
-(`roofline.achievable`, from the read probe); the sparse kernel over its
-load-only twin; measurement probes (read ceiling, launch floor); a parity
+(`roofline.achievable`, from the read probe), its duration taken from the
+graph of its launches (an event pair around every launch adds its marker
+packets to the launch); the sparse kernel over its load-only twin; measurement probes (read ceiling, launch floor); a parity
 summary of the timed outputs on sampled (batch row, KV head) units against
 the float64 oracle; the oracle itself timed on the host cores
 (`cpu_baseline`); comparison schedules, selection variants and a multi-token
@@ -422,10 +424,28 @@ class WorkloadRun:
 
             self.step()
             us = self.b.graph_time(one, len(s_layers))
-            res["sparse_layer"]["back_to_back_us"] = round(us, 2)
-            res["sparse_layer"]["back_to_back_GB_per_s"] = round(self.layer_bytes["attn_sparse"] / us / 1e3, 1)
-            res["sparse_layer"]["back_to_back_timing"] = "the step's sparse layers through ppsa_sparse_attn " \
-                                                         "(kernel and merge launch), captured in a graph"
+            nbytes = self.layer_bytes["attn_sparse"]
+            rec = res["sparse_layer"]
+            rec["back_to_back_us"] = round(us, 2)
+            rec["back_to_back_GB_per_s"] = round(nbytes / us / 1e3, 1)
+            rec["back_to_back_timing"] = "the step's sparse layers through ppsa_sparse_attn (kernel and merge " \
+                                         "launch), captured in a graph"
+
+            # The same layers' two launches apart (ppsa_sparse_attn_phases): the attention kernel alone, then
+            # the merge launch alone, each back to back in a graph.
+            def phase(ph):
+                def run_one(i):
+                    layer = s_layers[i % len(s_layers)]
+                    ppsa.sparse_attn(self.q[layer], self.k[layer], self.v[layer], self.lens,
+                                     self.idx[sel_of[layer]], out=outs[layer], workspace=self.ws, phases=ph)
+                return run_one
+
+            k_us = self.b.graph_time(phase(ppsa.PHASE_ATTN), len(s_layers))
+            rec["kernel_back_to_back_us"] = round(k_us, 2)
+            rec["kernel_back_to_back_GB_per_s"] = round(nbytes / k_us / 1e3, 1)
+            if sparse_merged:
+                rec["merge_back_to_back_us"] = round(self.b.graph_time(phase(ppsa.PHASE_MERGE), len(s_layers)), 2)
+            self.step()
         return res
 
     def gather_twin(self):
@@ -533,8 +553,10 @@ class WorkloadRun:
                "kernels": kernels, "layers_timed": self.layer_times(kernels)}
         if with_twin:
             twin = self.gather_twin()
-            if twin and "attn_sparse" in kernels:
-                twin["sparse_kernel_over_twin"] = round(kernels["attn_sparse"]["us_per_launch"] / twin["us_per_launch"], 3)
+            sl = rec["layers_timed"].get("sparse_layer", {})
+            if twin and "kernel_back_to_back_us" in sl:
+                twin["sparse_kernel_over_twin"] = round(sl["kernel_back_to_back_us"] / twin["us_per_launch"], 3)
+                twin["ratio_timing"] = "both back to back in a graph over the step's sparse layers"
             rec["gather_twin"] = twin
         rec["parity"] = self.parity()
         return rec
@@ -684,12 +706,24 @@ def main():
     dom = max(attn_keys, key=lambda kk: kernels[kk]["us_per_step"])
     traffic, traffic_src = measured_traffic(wl.name, dom)
     achievable = None if probes is None else probes["read_4GiB_nontemporal"]["GB_per_s"]
+    # Launch duration: for the sparse kernel the graph-timed back-to-back figure (events around the replay of
+    # the step's sparse launches, on the launch stream); the library's per-launch event pairs add the cost of
+    # their own marker packets to every launch and are reported beside it.
+    nbytes = run.layer_bytes[dom]
+    sl = rec["layers_timed"].get("sparse_layer", {})
+    if dom == "attn_sparse" and "kernel_back_to_back_us" in sl:
+        us_launch, timing_src = sl["kernel_back_to_back_us"], "graph of the step's sparse attention launches " \
+                                "(ppsa_sparse_attn_phases, attention phase), back to back, events around the replay"
+    else:
+        us_launch, timing_src = kernels[dom]["us_per_launch"], "library launch timing (events around each launch)"
+    achieved = round(nbytes / us_launch / 1e3, 1)
     roofline = {"bound": "hbm", "kernel": f"{dom}: {bench.ppsa.timing_kernel_name(bench.ppsa.KERNEL_KEYS.index(dom))}",
-                "achieved": kernels[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": kernels[dom]["hbm_frac"], "traffic": traffic, "traffic_source": traffic_src,
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
                 "achievable": achievable,
-                "frac_of_achievable": None if achievable is None else round(kernels[dom]["GB_per_s"] / achievable, 4),
-                "bytes_per_launch": run.layer_bytes[dom], "us_per_launch": kernels[dom]["us_per_launch"],
+                "frac_of_achievable": None if achievable is None else round(achieved / achievable, 4),
+                "bytes_per_launch": nbytes, "us_per_launch": us_launch, "us_per_launch_timing": timing_src,
+                "us_per_launch_event_pairs": kernels[dom]["us_per_launch"],
                 "launches_per_step": kernels[dom]["launches_per_step"]}
     layer_key = {"attn_sparse": "sparse_layer", "attn_full": "full_layer"}.get(dom)
     if layer_key and layer_key in rec["layers_timed"]:
@@ -742,7 +776,7 @@ def main():
         "config": {"workload": wl.name, "layers": wl.layers, "batch": wl.batch, "q_heads": wl.q_heads,
                    "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "seq_len": wl.max_len, "topk": wl.topk,
                    "select_layers": list(wl.select_layers), "parallelism": "single GPU"},
-        "timing": "value and ms_per_step: median of the steps, each timed after a 1 GiB cache-evicting write; "
+        "timing": "value and ms_per_step: median of the steps, each timed after a 1 GiB cache-evicting read; "
                   "step_us_back_to_back: the same steps without eviction",
         "step_us": rec["step_us"],
         "step_us_evicted": rec["step_us_evicted"],

@@ -165,6 +165,25 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * ppsa_sparse_attn as its two launches, for callers that place or time them
+ * apart. `phases` is a bitwise OR of:
+ *   PPSA_PHASE_ATTN   the attention launch: with one split per (b, kv) unit it
+ *                     writes out itself; otherwise it leaves each split's
+ *                     partial (max, normaliser, weighted V sum) in workspace;
+ *   PPSA_PHASE_MERGE  the merge launch: turns the partials in workspace into
+ *                     out (nothing to do, and no launch, with one split).
+ * PPSA_PHASE_ATTN | PPSA_PHASE_MERGE is ppsa_sparse_attn. A merge-only call
+ * takes the same arguments as the attention call it completes (same dims,
+ * topk and workspace; the plan, hence the partial layout, follows from them)
+ * and merges whatever that workspace holds. Errors as ppsa_sparse_attn, plus
+ * PPSA_ERR_INVALID_ARG for phases outside 1..3.
+ */
+enum { PPSA_PHASE_ATTN = 1, PPSA_PHASE_MERGE = 2 };
+int ppsa_sparse_attn_phases(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int32_t* idx, int32_t topk, int32_t phases, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step over `num_layers` layers (section 3 framework figure):
  * layer l runs the kind schedule[l] (host array of ppsa_layer_kind values)
  * on q[l], K[l], V[l] and writes out[l]. A PPSA_FULL_SELECT layer writes the

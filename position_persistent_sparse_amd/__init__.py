@@ -63,6 +63,7 @@ def _load():
     lib.ppsa_decode_step_ex.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp, vp, sz,
                                         vp]
     lib.ppsa_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.ppsa_sparse_attn_phases.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.ppsa_decode_step.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.ppsa_append_kv.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ppsa_decode_step_static.argtypes = [dp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
@@ -75,6 +76,7 @@ def _load():
     lib.ppsa_timing_kernel_name.argtypes = [i32]
     lib.ppsa_timing_kernel_name.restype = ctypes.c_char_p
     for name in ("ppsa_full_attn", "ppsa_full_attn_select", "ppsa_select_topk", "ppsa_sparse_attn",
+                 "ppsa_sparse_attn_phases",
                  "ppsa_decode_step", "ppsa_append_kv", "ppsa_timing_enable", "ppsa_timing_read",
                  "ppsa_select_topk_ex", "ppsa_decode_step_ex", "ppsa_decode_step_static", "ppsa_set_split_rows",
                  "ppsa_probe_read",
@@ -207,7 +209,15 @@ def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: s
     return idx
 
 
-def sparse_attn(q, k_cache, v_cache, seq_lens, idx, out=None, workspace=None, scale: float = 0.0):
+PHASE_ATTN = 1
+PHASE_MERGE = 2
+
+
+def sparse_attn(q, k_cache, v_cache, seq_lens, idx, out=None, workspace=None, scale: float = 0.0,
+                phases: int = PHASE_ATTN | PHASE_MERGE):
+    """Sparse attention over idx [B, Hkv, topk]. `phases` picks the attention launch, the merge launch or both
+    (ppsa_sparse_attn_phases); a merge-only call completes an attention-only call on the same workspace."""
+    _require(phases in (1, 2, 3), "phases must be PHASE_ATTN, PHASE_MERGE or both")
     _check_tensors(q, k_cache, v_cache, seq_lens)
     dims = _dims_of(q, k_cache, scale)
     _require(idx.dtype == torch.int32 and idx.is_contiguous() and idx.dim() == 3
@@ -217,9 +227,10 @@ def sparse_attn(q, k_cache, v_cache, seq_lens, idx, out=None, workspace=None, sc
     out = torch.empty_like(q) if out is None else out
     _check_buffer(out, q.shape, q.dtype, q.device, "out")
     ws = alloc_workspace(dims, topk, q.device) if workspace is None else workspace
-    _check(_lib.ppsa_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
-                                 _ptr(idx), int(topk), _ptr(out), _ptr(ws), _workspace_nbytes(ws, q.device),
-                                 _stream(q.device)), "ppsa_sparse_attn")
+    _check(_lib.ppsa_sparse_attn_phases(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                        _ptr(idx), int(topk), int(phases), _ptr(out), _ptr(ws),
+                                        _workspace_nbytes(ws, q.device), _stream(q.device)),
+           "ppsa_sparse_attn_phases")
     return out
 
 

@@ -1,6 +1,6 @@
-// Merge of one (batch row, query head)'s split partials by one 64-lane wave (gfx950); used by the
-// merge pass (combine.hip) and by the selection launch, which merges a selection layer's rows in
-// extra workgroups beside the top-k work.
+// Merge of one (batch row, query head)'s split partials by one 64-lane wave (gfx950), used by the
+// selection launch, which merges a selection layer's rows in extra workgroups beside the top-k work
+// (the merge pass of the other layers, combine.hip, spreads each row over a workgroup instead).
 //
 // Each split s leaves m_s (max logit, log2 units), l_s = sum 2^(x - m_s) and o_s = sum
 // 2^(x - m_s) V[row]. The softmax over the union of the splits is

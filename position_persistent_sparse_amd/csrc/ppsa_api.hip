@@ -271,17 +271,19 @@ int run_full(const Ctx& c, const void* q, const void* k, const void* v, const in
 }
 
 int run_sparse(const Ctx& c, const void* q, const void* k, const void* v, const int32_t* seq_lens,
-               const int32_t* idx, int topk, void* out) {
+               const int32_t* idx, int topk, void* out, int phases = PPSA_PHASE_ATTN | PPSA_PHASE_MERGE) {
   AttnArgs a = base_args(c, q, k, v, seq_lens, out);
   a.idx = idx;
   a.kslots = topk;
   a.splits = c.plan.sparse_splits;
   a.rows_per_split = c.plan.sparse_rows;
   a.idx_vec = (topk % 4 == 0 && aligned(idx, 16)) ? 1 : 0;
-  const int rc = finish(timed(KERNEL_ATTN_SPARSE, c.stream, [&] {
-    return c.plan.mfma ? launch_attn_sparse(a, c.stream) : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream);
-  }));
-  return rc == PPSA_OK ? run_combine(c, a.splits, out) : rc;
+  int rc = PPSA_OK;
+  if (phases & PPSA_PHASE_ATTN)
+    rc = finish(timed(KERNEL_ATTN_SPARSE, c.stream, [&] {
+      return c.plan.mfma ? launch_attn_sparse(a, c.stream) : launch_attn(a, MODE_SPARSE, c.d->dtype, c.d->head_dim, c.stream);
+    }));
+  return rc == PPSA_OK && (phases & PPSA_PHASE_MERGE) ? run_combine(c, a.splits, out) : rc;
 }
 
 // Pointer and workspace checks common to the attention entry points.
@@ -403,6 +405,14 @@ int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_
 int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* seq_lens, const int32_t* idx, int32_t topk, void* out, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  return ppsa_sparse_attn_phases(dims, q, k_cache, v_cache, seq_lens, idx, topk, PPSA_PHASE_ATTN | PPSA_PHASE_MERGE,
+                                 out, workspace, workspace_bytes, stream);
+}
+
+int ppsa_sparse_attn_phases(const ppsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int32_t* idx, int32_t topk, int32_t phases, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (phases < 1 || phases > (PPSA_PHASE_ATTN | PPSA_PHASE_MERGE)) return PPSA_ERR_INVALID_ARG;
   int rc = check_dims(dims);
   if (rc != PPSA_OK) return rc;
   if ((rc = check_topk(dims, topk)) != PPSA_OK) return rc;
@@ -413,7 +423,7 @@ int ppsa_sparse_attn(const ppsa_dims* dims, const void* q, const void* k_cache, 
   if (!c.plan.sparse_ok) return PPSA_ERR_UNSUPPORTED;
   if (workspace_bytes < c.plan.total) return PPSA_ERR_WORKSPACE;
   (void)hipGetLastError();
-  return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out);
+  return run_sparse(c, q, k_cache, v_cache, seq_lens, idx, topk, out, phases);
 }
 
 int ppsa_append_kv(const ppsa_dims* dims, int32_t num_layers, const void* k_new, const void* v_new,

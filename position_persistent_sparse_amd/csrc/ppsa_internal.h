@@ -111,7 +111,7 @@ hipError_t launch_empty_probe(int groups, int threads, int32_t* sink, hipStream_
 hipError_t launch_gather_twin(const AttnArgs& a, int32_t* sink, hipStream_t stream);
 // Largest group size the attention kernels take.
 constexpr int kMaxGroup = 16;
-// Most splits one unit may be cut into (the merge pass keeps one weight per split in LDS).
+// Most splits one unit may be cut into.
 constexpr int kMaxSplitsPerUnit = 256;
 
 // Append of one token's K/V rows (append.hip): rows [L, B, Hkv] of row_bytes each go to position

@@ -111,6 +111,21 @@ def test_topk_range():
     assert LIB.ppsa_select_topk(ctypes.byref(d), FAKE, FAKE, 1001, FAKE, None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG
 
 
+def test_sparse_phases_validation():
+    d = dims()
+    wsb = ppsa.workspace_bytes(d, 16)
+
+    def phases(ph, idx=FAKE, ws_bytes=wsb):
+        return LIB.ppsa_sparse_attn_phases(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, idx, 16, ph, FAKE, FAKE,
+                                           ws_bytes, None)
+
+    for bad in (0, 4, -1):
+        assert phases(bad) == ppsa.PPSA_ERR_INVALID_ARG, bad
+    for ph in (1, 2, 3):
+        assert phases(ph, idx=None) == ppsa.PPSA_ERR_INVALID_ARG, ph
+        assert phases(ph, ws_bytes=wsb - 256) == ppsa.PPSA_ERR_WORKSPACE, ph
+
+
 def test_workspace_too_small():
     d = dims()
     assert full(d, ws_bytes=ppsa.workspace_bytes(d, 0) - 1) == ppsa.PPSA_ERR_WORKSPACE

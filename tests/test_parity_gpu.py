@@ -167,6 +167,26 @@ def test_sparse_with_k_equal_n_matches_full():
     assert np.abs(a - b).max() <= 2 ** -8 * np.abs(a).max() + 1e-6
 
 
+@pytest.mark.parametrize("topk", [96, 1000])
+def test_sparse_phases_compose_to_the_layer(topk):
+    """The attention launch and the merge launch called apart (ppsa_sparse_attn_phases) give the same bits
+    as the whole layer, with one split per unit (96 slots: the attention launch writes out itself) and with
+    several (1000 slots: the merge completes out)."""
+    wl = synth.WORKLOADS["llama3-8b-gqa-32k"].with_(layers=1, batch=2, q_heads=8, kv_heads=2, max_len=3000,
+                                                    topk=topk, select_layers=())
+    gen = synth.Generator(wl, seq_lens=[3000, 2222])
+    q, k, v, lens, _ = torch_io.upload(wl, gen, DEV)
+    rng = np.random.default_rng(12)
+    idx = torch.from_numpy(np.sort(rng.integers(0, 2222, size=(2, 2, topk)), axis=2).astype(np.int32)).to(DEV)
+    whole = ppsa.sparse_attn(q[0], k[0], v[0], lens, idx)
+    ws = ppsa.alloc_workspace(ppsa.make_dims(2, 8, 2, 128, 3000, torch.bfloat16), topk, torch.device(DEV))
+    out = torch.full_like(q[0], float("nan"))
+    ppsa.sparse_attn(q[0], k[0], v[0], lens, idx, out=out, workspace=ws, phases=ppsa.PHASE_ATTN)
+    ppsa.sparse_attn(q[0], k[0], v[0], lens, idx, out=out, workspace=ws, phases=ppsa.PHASE_MERGE)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+
+
 def test_sparse_invalid_and_repeated_entries():
     wl = synth.WORKLOADS["tiny-f32"].with_(layers=1, batch=1, q_heads=4, kv_heads=2, max_len=300, topk=40,
                                            select_layers=())
