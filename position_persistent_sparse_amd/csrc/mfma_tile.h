@@ -8,13 +8,16 @@
 //   S^T[row, head] = K[row, :] . q[head, :]
 //       v_mfma_f32_16x16x32_bf16, A = K (lane%16 = row, lane/16 picks 8 of each 32 dims), B = q
 //       (lane%16 = head); four products cover d = 128.
-//   The result leaves lane (g = lane/16, n = lane%16) holding the logits of rows 4g..4g+3 for head
-//   n, which is exactly the A operand layout of v_mfma_f32_16x16x16_bf16 for P[head, row] over
-//   those 16 rows, so the softmax weights never leave the lane.
+//   The result leaves lane (g = lane/16, n = lane%16) holding the logits of rows 4g..4g+3 of each
+//   block for head n: eight rows of the tile, 4g..4g+3 and 16+4g..16+4g+3. The contraction index
+//   of a product may be numbered in any order both operands share, so those eight rows are the
+//   lane's eight k slots of one v_mfma_f32_16x16x32_bf16 over the whole 32-row tile, with
+//   A = P[head, row]: the softmax weights never leave the lane.
 //   O[head, dim] += P[head, :] . V[:, dim]
-//       B = V needs rows along the operand elements: lane (g, n) holds rows 4g..4g+3 at dims
+//       B = V needs the same eight rows along the operand elements: lane (g, n) holds them at dims
 //       8n..8n+7 (16 lanes cover a whole 256-byte row) and product t uses dim 8n+t of each,
-//       regrouped with v_perm_b32. The output column n of product t is dim 8n+t.
+//       regrouped with v_perm_b32. The output column n of product t is dim 8n+t; eight products
+//       per tile.
 // The running max is shared by the four lanes holding a head (a max across the wave's four rows
 // per tile) and only moved when a tile exceeds it by more than 2^8 ("lazy" rescaling: weights may reach 256, still
 // exact in the float32 sums); a merge uses each partial's own max, so the result is the same
@@ -30,7 +33,6 @@ namespace ppsa {
 namespace mt {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -173,20 +175,25 @@ __device__ __forceinline__ void softmax_pv(const Tile& t, const float (&x)[2][4]
     st.m_run = m_new;
   }
   const float ms = st.m_run == -INFINITY ? 0.0f : st.m_run;
+  // k slots 0..3: rows 4g..4g+3 of block 0; slots 4..7: the same rows of block 1.
+  uint32_t p[2][2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const uint32_t p01 = bf16_pair(exp2_fast(x[blk][0] - ms), exp2_fast(x[blk][1] - ms));
-    const uint32_t p23 = bf16_pair(exp2_fast(x[blk][2] - ms), exp2_fast(x[blk][3] - ms));
-    st.l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-    const short4_t pa = __builtin_bit_cast(short4_t, make_uint2(p01, p23));
+    p[blk][0] = bf16_pair(exp2_fast(x[blk][0] - ms), exp2_fast(x[blk][1] - ms));
+    p[blk][1] = bf16_pair(exp2_fast(x[blk][2] - ms), exp2_fast(x[blk][3] - ms));
+    st.l_run += (bf16_lo(p[blk][0]) + bf16_hi(p[blk][0])) + (bf16_lo(p[blk][1]) + bf16_hi(p[blk][1]));
+  }
+  const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]));
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t d0 = __builtin_amdgcn_perm(word(t.v[blk][1], tt >> 1), word(t.v[blk][0], tt >> 1), sel);
-      const uint32_t d1 = __builtin_amdgcn_perm(word(t.v[blk][3], tt >> 1), word(t.v[blk][2], tt >> 1), sel);
-      const short4_t vbv = __builtin_bit_cast(short4_t, make_uint2(d0, d1));
-      st.acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vbv, st.acc[tt], 0, 0, 0);
-    }
+  for (int tt = 0; tt < 8; ++tt) {
+    const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
+    const int w = tt >> 1;
+    const uint32_t d0 = __builtin_amdgcn_perm(word(t.v[0][1], w), word(t.v[0][0], w), sel);
+    const uint32_t d1 = __builtin_amdgcn_perm(word(t.v[0][3], w), word(t.v[0][2], w), sel);
+    const uint32_t d2 = __builtin_amdgcn_perm(word(t.v[1][1], w), word(t.v[1][0], w), sel);
+    const uint32_t d3 = __builtin_amdgcn_perm(word(t.v[1][3], w), word(t.v[1][2], w), sel);
+    const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(d0, d1, d2, d3));
+    st.acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, st.acc[tt], 0, 0, 0);
   }
 }
 
