@@ -67,7 +67,8 @@ def parse():
     p.add_argument("--no-probes", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-probe", action="store_true", help="also time a plain 1 GiB device copy (PMC calibration)")
-    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (counter-collection runs)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip every timing taken through a captured graph (counter-collection runs)")
     p.add_argument("--no-comparison", action="store_true", help="skip the dense and select-every-layer schedules")
     p.add_argument("--no-multi-token", action="store_true", help="skip the multi-token (append + step) timing")
     return p.parse_args()
@@ -404,6 +405,7 @@ class WorkloadRun:
                                       "(whose launch also merges the layer's partials)"}
         if "attn_sparse" in kernels:
             us = kernels["attn_sparse"]["us_per_launch"] + (comb_us if sparse_merged else 0.0)
+            graphs = not self.b.args.no_graph
             res["sparse_layer"] = {"events_us": round(us, 2), "merge_launch": sparse_merged,
                                    "GB_per_s": round(self.layer_bytes["attn_sparse"] / us / 1e3, 1),
                                    "hbm_frac": round(self.layer_bytes["attn_sparse"] / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -422,6 +424,8 @@ class WorkloadRun:
                 ppsa.sparse_attn(self.q[layer], self.k[layer], self.v[layer], self.lens, self.idx[sel_of[layer]],
                                  out=outs[layer], workspace=self.ws)
 
+            if not graphs:
+                return res
             self.step()
             us = self.b.graph_time(one, len(s_layers))
             nbytes = self.layer_bytes["attn_sparse"]
@@ -551,7 +555,7 @@ class WorkloadRun:
                "step_us_with_launch_timing": round(instrumented, 1),
                "selection_overhead_frac": round(sel_us / med, 4),
                "kernels": kernels, "layers_timed": self.layer_times(kernels)}
-        if with_twin:
+        if with_twin and not self.b.args.no_graph:
             twin = self.gather_twin()
             sl = rec["layers_timed"].get("sparse_layer", {})
             if twin and "kernel_back_to_back_us" in sl:

@@ -131,26 +131,32 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
   __syncthreads();
 
   // Workgroup result: thread i < group * 32 takes head i / 32, dims 4 (i % 32) .. +3, and combines
-  // the waves with their weights 2^(m_w - M).
+  // the waves with their weights 2^(m_w - M). group * 32 <= 512 items: at most two per thread.
   const int nq = group * (kD / 4);
-  uint16_t* outg = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)kv * group) * kD;
-  for (int i = tid; i < nq; i += kThreads) {
+  const size_t row0 = (size_t)b * a.q_heads + (size_t)kv * group;  // (b, first head of the group)
+  auto combine = [&](int i) {
     const int h = i >> 5, d = (i & 31) * 4;
-    float mx = -INFINITY;
+    float mw[WAVES], mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 0; w < WAVES; ++w) {
+      mw[w] = sm_m[w][h];
+      mx = fmaxf(mx, mw[w]);
+    }
+    float4_t ow[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) ow[w] = *reinterpret_cast<const float4_t*>(dyn + w * wstride + h * kORow + d);
     const float ms = mx == -INFINITY ? 0.0f : mx;
     float l = 0.0f;
     float4_t o = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
-      const float c = exp2_fast(sm_m[w][h] - ms);
+      const float c = exp2_fast(mw[w] - ms);
       l += sm_l[w][h] * c;
-      o += *reinterpret_cast<const float4_t*>(dyn + w * wstride + h * kORow + d) * c;
+      o += ow[w] * c;
     }
     if (S == 1) {
-      store_out4(outg + (size_t)h * kD + d, o, l > 0.0f ? 1.0f / l : 0.0f);
-      continue;
+      store_out4(reinterpret_cast<uint16_t*>(a.out) + (row0 + h) * kD + d, o, l > 0.0f ? 1.0f / l : 0.0f);
+      return;
     }
     const size_t row = part_row(a, b, kv, h, split);
     *reinterpret_cast<float4_t*>(a.part_o + row * kD + d) = o;
@@ -158,7 +164,9 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
       a.part_m[row] = mx;
       a.part_l[row] = l;
     }
-  }
+  };
+  if (tid < nq) combine(tid);
+  if (kThreads < kMaxGroup * (kD / 4) && tid + kThreads < nq) combine(tid + kThreads);
 }
 
 template <int WAVES, bool STREAM>
