@@ -400,9 +400,10 @@ class WorkloadRun:
             res["full_layer"] = {"events_us": round(us, 2), "merge_launch": full_merged,
                                  "GB_per_s": round(self.layer_bytes["attn_full"] / us / 1e3, 1)}
         if "attn_full_scores" in kernels and "select" in kernels:
-            us = kernels["attn_full_scores"]["us_per_launch"] + kernels["select"]["us_per_launch"]
+            us = kernels["attn_full_scores"]["us_per_launch"] + kernels["select"]["us_per_step"] / max(self.n_sel, 1)
             res["selection_layer"] = {"events_us": round(us, 2), "note": "attention + score write, then top-k "
-                                      "(whose launch also merges the layer's partials)"}
+                                      "(whose first launch also merges the layer's partials; rows over 32768 "
+                                      "positions take two selection launches)"}
         if "attn_sparse" in kernels:
             us = kernels["attn_sparse"]["us_per_launch"] + (comb_us if sparse_merged else 0.0)
             graphs = not self.b.args.no_graph

@@ -113,7 +113,12 @@ int ppsa_full_attn_select(const ppsa_dims* dims, const void* q, const void* k_ca
 /*
  * Token selection alone, on given scores [B, Hkv, Nmax] (float32, only the
  * live entries are read): writes idx exactly as ppsa_full_attn_select does.
- * Scores must not be NaN. -0.0 ranks equal to +0.0.
+ * Scores must not be NaN. -0.0 ranks equal to +0.0. The workspace is
+ * optional (NULL with workspace_bytes 0): given one of at least
+ * ppsa_workspace_bytes(dims, topk) bytes, 16-byte aligned, per-KV-head sets
+ * of rows longer than 65536 positions are chosen in two launches (top-k of
+ * each chunk of the row, then top-k of the chunks' winners: the same set)
+ * when the chunks' winners fit 32768 entries; otherwise in one.
  */
 int ppsa_select_topk(const ppsa_dims* dims, const float* scores, const int32_t* seq_lens, int32_t topk,
                      int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);

@@ -194,8 +194,11 @@ def full_attn_select(q, k_cache, v_cache, seq_lens, topk: int, out=None, scores=
     return out, idx
 
 
-def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: str = "kv_head"):
-    """Top-k per (batch row, KV head), or per batch row over the KV heads' summed scores (mode "shared")."""
+def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: str = "kv_head",
+                workspace=None, two_stage: bool = True):
+    """Top-k per (batch row, KV head), or per batch row over the KV heads' summed scores (mode "shared").
+    With `two_stage` (default) a workspace is passed (allocated when not given), so that long rows are
+    selected in two launches; two_stage=False passes none (one launch)."""
     _require(scores.dim() == 3 and scores.dtype == torch.float32 and scores.is_contiguous() and scores.is_cuda,
              "scores must be contiguous float32 [B, Hkv, N] on the GPU")
     B, Hkv, N = scores.shape
@@ -204,8 +207,12 @@ def select_topk(scores, seq_lens, topk: int, idx=None, num_q_heads=None, mode: s
     if idx is None:
         idx = torch.empty((B, Hkv, int(topk)), dtype=torch.int32, device=scores.device)
     _check_buffer(idx, (B, Hkv, int(topk)), torch.int32, scores.device, "idx")
+    ws = None
+    if two_stage:
+        ws = alloc_workspace(dims, topk, scores.device) if workspace is None else workspace
     _check(_lib.ppsa_select_topk_ex(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), int(topk), SELECT_MODES[mode],
-                                    _ptr(idx), None, 0, _stream(scores.device)), "ppsa_select_topk_ex")
+                                    _ptr(idx), _ptr(ws), 0 if ws is None else _workspace_nbytes(ws, scores.device),
+                                    _stream(scores.device)), "ppsa_select_topk_ex")
     return idx
 
 

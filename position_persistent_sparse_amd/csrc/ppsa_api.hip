@@ -65,6 +65,8 @@ struct Plan {
   size_t off_m = 0, off_l = 0, off_o = 0, off_scores = 0, total = 0;
   size_t off_heads = 0, off_fm = 0, off_fl = 0;  // softmax-weight selection: head logits, final max / sum
   size_t off_unitk = 0;                           // coverage budget per unit
+  size_t off_cand_score = 0, off_cand_pos = 0;    // two-stage selection: candidate rows
+  int sel_chunk = 0, sel_nchunks = 0, sel_stride = 0;  // two-stage selection geometry (0: one launch)
   bool full_ok = true;    // false: full layers would need more splits than one unit may have
   bool sparse_ok = true;  // false: the budget needs more splits than one unit may have
   bool mfma = false;
@@ -129,6 +131,12 @@ Plan make_plan(const ppsa_dims& d, int topk, bool variants = true, bool score_bu
     p.off_fm = off; off = align_up(off + heads * sizeof(float));
     p.off_fl = off; off = align_up(off + heads * sizeof(float));
     p.off_unitk = off; off = align_up(off + (size_t)std::max(d.batch, 0) * d.num_kv_heads * sizeof(int32_t));
+  }
+  if (topk > 0 && select_two_stage(d.max_seq_len, topk, &p.sel_chunk, &p.sel_nchunks)) {
+    p.sel_stride = (int)round_up((int64_t)p.sel_nchunks * topk, 4);
+    const size_t cand = (size_t)std::max(d.batch, 0) * d.num_kv_heads * p.sel_stride;
+    p.off_cand_score = off; off = align_up(off + cand * sizeof(float));
+    p.off_cand_pos = off; off = align_up(off + cand * sizeof(int32_t));
   }
   p.total = off;
   return p;
@@ -211,6 +219,22 @@ int run_select(const Ctx& c, const float* scores, const int32_t* seq_lens, int t
   s.kv_heads = c.d->num_kv_heads;
   s.max_len = c.d->max_seq_len;
   s.topk = topk;
+  // Long rows of per-KV-head sets: top-k per chunk of the row, then over the chunks' winners (two
+  // launches, the first spread over chunks x units workgroups). Needs the workspace's candidate rows.
+  if (mode == PPSA_SELECT_PER_KV_HEAD && !unit_k && c.ws && c.plan.sel_nchunks > 0) {
+    s.chunk = c.plan.sel_chunk;
+    s.nchunks = c.plan.sel_nchunks;
+    s.cand_stride = c.plan.sel_stride;
+    s.cand_score = reinterpret_cast<float*>(c.ws + c.plan.off_cand_score);
+    s.cand_pos = reinterpret_cast<int32_t*>(c.ws + c.plan.off_cand_pos);
+    s.stage = 1;
+    int rc = finish(timed(KERNEL_SELECT, c.stream, [&] {
+      return merge ? launch_select_merge(s, *merge, c.stream) : launch_select(s, c.stream);
+    }));
+    if (rc != PPSA_OK) return rc;
+    s.stage = 2;
+    return finish(timed(KERNEL_SELECT, c.stream, [&] { return launch_select(s, c.stream); }));
+  }
   return finish(timed(KERNEL_SELECT, c.stream, [&] {
     return merge ? launch_select_merge(s, *merge, c.stream) : launch_select(s, c.stream);
   }));
@@ -397,7 +421,9 @@ int ppsa_select_topk_ex(const ppsa_dims* dims, const float* scores, const int32_
   if (!scores || !seq_lens || !idx || !aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(idx, 4))
     return PPSA_ERR_INVALID_ARG;
   if (workspace_bytes > 0 && !workspace) return PPSA_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 16)) return PPSA_ERR_INVALID_ARG;
   Ctx c{dims, make_plan(*dims, topk), static_cast<char*>(workspace), static_cast<hipStream_t>(stream)};
+  if (workspace_bytes < c.plan.total) c.ws = nullptr;  // one launch: no room for the candidate rows
   (void)hipGetLastError();
   return run_select(c, scores, seq_lens, topk, idx, select_mode);
 }

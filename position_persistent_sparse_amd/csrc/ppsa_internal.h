@@ -65,6 +65,17 @@ struct SoftmaxScoreArgs {
 };
 hipError_t launch_softmax_scores(const SoftmaxScoreArgs& a, hipStream_t stream);
 
+// Stages of a selection (per (batch row, KV head) sets only; 0 for the others):
+//   0  one launch: each unit's whole row;
+//   1  each unit's row cut into `nchunks` chunks of `chunk` positions, one workgroup each: the top
+//      min(topk, live positions of the chunk) of the chunk go, as (score, position) in position
+//      order, to the unit's candidate row at the offset of the chunk (the kept counts of the chunks
+//      before it, a closed form of the live length);
+//   2  each unit's candidate row (its live length is the sum of the chunks' kept counts): top-k,
+//      the positions read back from the candidate row.
+// Every position of the global top-k is in its chunk's top-k (fewer than k positions of the whole
+// row rank above it, hence fewer than k of its chunk), and candidates sit in position order, so
+// stage 2 over the candidates picks exactly the set stage 0 picks over the row, ties included.
 struct SelectArgs {
   const float* scores;      // [B, Hkv, Nmax]
   const int32_t* seq_lens;  // [B]
@@ -72,7 +83,16 @@ struct SelectArgs {
   int32_t batch, kv_heads, max_len, topk;
   int32_t shared;           // 1: one set per batch row over the sum of its KV heads' scores
   const int32_t* unit_k;    // optional [units]: per-unit budget (capped by topk)
+  int32_t stage;            // 0, 1 or 2 (above)
+  int32_t chunk, nchunks;   // stages 1 and 2: chunk length (a multiple of 4) and chunks per row
+  int32_t cand_stride;      // stages 1 and 2: candidate row length per unit (>= nchunks * topk, multiple of 4)
+  float* cand_score;        // stages 1 and 2: [B * Hkv, cand_stride]
+  int32_t* cand_pos;        // stages 1 and 2: [B * Hkv, cand_stride]
 };
+// Two-stage plan for rows of max_len positions and top-k (per-KV-head sets): chunk length and count,
+// or false when one launch is used (rows of at most two super-rounds of 32768 positions, or a
+// candidate row longer than one).
+bool select_two_stage(int max_len, int topk, int* chunk, int* nchunks);
 
 // Coverage budget (coverage.hip): per (b, kv) unit, with masses m_n = scores[unit, n] / group (the
 // group's softmax-weight sums, total ~1), the number of positions kept once the lowest-mass tail is

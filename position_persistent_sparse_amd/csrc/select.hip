@@ -9,8 +9,9 @@
 // and instruction issue on that one CU, so every step keeps the per-score
 // work to a few instructions and avoids per-score branches. Positions are taken in
 // super-rounds of up to 32768: in super-round r thread t owns per_r
-// contiguous positions (per_r = ceil(n_r / 1024) <= 32, loaded 16 bytes at a
-// time when aligned), so position order is (super-round, thread, bit). Each score maps to an
+// contiguous positions (per_r = ceil(n_r / 1024) rounded up to a multiple of
+// 4, <= 32, loaded 16 bytes at a time when aligned), so position order is
+// (super-round, thread, bit). Each score maps to an
 // order-preserving 32-bit key (-0.0 folded onto +0.0): ranking floats is
 // ranking unsigned integers.
 //  1. Radix digit 1 (key bits 31..21) over all keys: an LDS histogram (in
@@ -30,6 +31,13 @@
 // longer rows reload their super-rounds in each step, except that rows of up
 // to four super-rounds take step 3 from masks kept by step 2 (two reads of
 // the scores instead of three).
+//
+// Rows of more than two super-rounds may instead be taken in two launches
+// (SelectArgs::stage): the same kernel first runs on chunks of the row, one
+// workgroup per (unit, chunk), each keeping its chunk's top-k as (score,
+// position) in a candidate row, then on each unit's candidate row. Each
+// launch costs its serial phases once; from three chunks up the parallel
+// first stage more than pays for the second launch.
 #include <math.h>
 
 #include "combine_row.h"
@@ -98,7 +106,7 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, uint32_t count) {
 template <bool CACHED, bool SHARED, bool MERGE>
 __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, CombineArgs c) {
   if constexpr (MERGE) {
-    const int units = SHARED ? a.batch : a.batch * a.kv_heads;
+    const int units = (SHARED ? a.batch : a.batch * a.kv_heads) * (!SHARED && a.stage == 1 ? a.nchunks : 1);
     if ((int)blockIdx.x >= units) {
       const int row = ((int)blockIdx.x - units) * kWaves + (int)threadIdx.x / kWave;
       const int ln = (int)threadIdx.x % kWave;
@@ -120,38 +128,84 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   __shared__ uint32_t cand[kMaxCand];
   __shared__ uint32_t s_digit, s_above;
 
-  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid % kWave;
+  const int stage = SHARED ? 0 : a.stage;
+  const int nch = stage == 1 ? a.nchunks : 1;
+  const int unit = (int)blockIdx.x / nch, chunk_i = (int)blockIdx.x - unit * nch;
+  const int tid = threadIdx.x, lane = tid % kWave;
   const int b = SHARED ? unit : unit / a.kv_heads;
-  const int n = min(max(a.seq_lens[b], 0), a.max_len);
-  int k_eff = min(a.topk, n);
-  if (a.unit_k) k_eff = min(k_eff, max(a.unit_k[unit], 0));  // per-unit budget (coverage variant)
-  // Score rows summed per position (all KV heads of the batch row when SHARED) and idx rows written.
+  const int n_live = min(max(a.seq_lens[b], 0), a.max_len);
+  // Kept count of chunk c (stages 1 and 2).
+  auto chunk_keep = [&](int c) { return min(a.topk, min(max(n_live - c * a.chunk, 0), a.chunk)); };
+  // The row this workgroup ranks: `n` live scores from `s` (summed over all KV heads of the batch row
+  // when SHARED), `pitch` apart between rows, and where the kept positions go.
   const int rows = SHARED ? a.kv_heads : 1;
-  const float* s = a.scores + (size_t)unit * rows * a.max_len;
+  const float* s;
+  int n, pitch, pos0 = 0;
+  float* cand_score = nullptr;
+  int32_t* cand_pos = nullptr;
+  const int32_t* pos_map = nullptr;
+  if (stage == 1) {
+    pos0 = chunk_i * a.chunk;
+    n = min(max(n_live - pos0, 0), a.chunk);
+    s = a.scores + (size_t)unit * a.max_len + pos0;
+    pitch = a.max_len;
+    int off = 0;
+    for (int c = 0; c < chunk_i; ++c) off += chunk_keep(c);
+    cand_score = a.cand_score + (size_t)unit * a.cand_stride + off;
+    cand_pos = a.cand_pos + (size_t)unit * a.cand_stride + off;
+  } else if (stage == 2) {
+    n = 0;
+    for (int c = 0; c < a.nchunks; ++c) n += chunk_keep(c);
+    s = a.cand_score + (size_t)unit * a.cand_stride;
+    pitch = a.cand_stride;
+    pos_map = a.cand_pos + (size_t)unit * a.cand_stride;
+  } else {
+    n = n_live;
+    s = a.scores + (size_t)unit * rows * a.max_len;
+    pitch = a.max_len;
+  }
+  int k_eff = min(a.topk, n);
+  if (stage == 0 && a.unit_k) k_eff = min(k_eff, max(a.unit_k[unit], 0));  // per-unit budget (coverage variant)
   int32_t* out = a.idx + (size_t)unit * rows * a.topk;
+  // Kept position `pos` of the row to output slot `slot`.
   auto emit = [&](uint32_t slot, int32_t pos) {
-    for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = pos;
+    if (stage == 1) {
+      cand_score[slot] = s[pos];
+      cand_pos[slot] = pos0 + pos;
+    } else {
+      const int32_t p = stage == 2 ? pos_map[pos] : pos;
+      for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = p;
+    }
+  };
+  // Output slots left empty (a chunk's candidate row has no such slots).
+  auto emit_empty = [&](uint32_t slot) {
+    if (stage != 1)
+      for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = -1;
   };
 
   if (k_eff == n || k_eff == 0) {  // every live position is kept, or none (includes n == 0)
-    for (int i = tid; i < a.topk; i += kThreads) emit(i, i < k_eff ? i : -1);
+    for (int i = tid; i < a.topk; i += kThreads) {
+      if (i < k_eff) emit(i, i);
+      else emit_empty(i);
+    }
     return;
   }
-  for (int i = k_eff + tid; i < a.topk; i += kThreads) emit(i, -1);  // slots past a per-unit budget
+  for (int i = k_eff + tid; i < a.topk; i += kThreads) emit_empty(i);  // slots past a per-unit budget
 
-  // Rows start 16-byte aligned when the base is and hold a multiple of 4 scores.
-  const bool aligned = (a.max_len % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) % 16) == 0;
+  // Rows start 16-byte aligned when their first score is and rows hold a multiple of 4 scores.
+  const bool aligned = (pitch % 4) == 0 && (reinterpret_cast<uintptr_t>(s) % 16) == 0;
   const int n_sr = (n + kPerSuper - 1) / kPerSuper;
-  // Super-round r spans n_r positions; thread t owns per_r = ceil(n_r / 1024) of them from
-  // p0(r, t) = 32768 r + t per_r. Loads this thread's keys (0 past its live ones) and the
-  // mask of the live ones.
+  // Super-round r spans n_r positions; thread t owns per_r of them from p0(r, t) = 32768 r + t per_r,
+  // per_r = ceil(n_r / 1024) rounded up to a multiple of 4 (so that full spans load 16 bytes at a
+  // time; the last threads may own fewer or none). Loads this thread's keys (0 past its live ones)
+  // and the mask of the live ones.
   struct Span {
     int p0, per;
     uint32_t live;
   };
   auto span_of = [&](int r) -> Span {
     const int n_r = min(kPerSuper, n - r * kPerSuper);
-    const int per = (n_r + kThreads - 1) / kThreads;
+    const int per = ((n_r + kThreads - 1) / kThreads + 3) & ~3;
     const int p0 = r * kPerSuper + tid * per;
     const int cnt = max(0, min(per, r * kPerSuper + n_r - p0));
     return Span{p0, per, cnt >= kCached ? 0xFFFFFFFFu : ((1u << cnt) - 1u)};
@@ -167,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
         if (4 * j < per) {
           float4 f = *reinterpret_cast<const float4*>(s + p0 + 4 * j);
           for (int r = 1; r < rows; ++r) {  // heads in order: the same float32 sum every time
-            const float4 g = *reinterpret_cast<const float4*>(s + (size_t)r * a.max_len + p0 + 4 * j);
+            const float4 g = *reinterpret_cast<const float4*>(s + (size_t)r * pitch + p0 + 4 * j);
             f.x += g.x;
             f.y += g.y;
             f.z += g.z;
@@ -185,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
           float f = 0.0f;
           if (i < cnt) {
             f = s[p0 + i];
-            for (int r = 1; r < rows; ++r) f += s[(size_t)r * a.max_len + p0 + i];
+            for (int r = 1; r < rows; ++r) f += s[(size_t)r * pitch + p0 + i];
           }
           k[i] = i < cnt ? order_key(f) : 0u;
         }
@@ -370,8 +424,10 @@ namespace {
 
 template <bool MERGE>
 void launch_select_kernel(const SelectArgs& a, const CombineArgs& c, int extra_blocks, hipStream_t stream) {
-  const dim3 grid((a.shared ? a.batch : a.batch * a.kv_heads) + extra_blocks), block(kThreads);
-  const bool cached = a.max_len <= kPerSuper;
+  const int groups = a.shared ? a.batch : a.batch * a.kv_heads * (a.stage == 1 ? a.nchunks : 1);
+  const dim3 grid(groups + extra_blocks), block(kThreads);
+  const int row_len = a.shared || a.stage == 0 ? a.max_len : (a.stage == 1 ? a.chunk : a.cand_stride);
+  const bool cached = row_len <= kPerSuper;
   if (a.shared) {
     if (cached) select_topk_kernel<true, true, MERGE><<<grid, block, 0, stream>>>(a, c);
     else select_topk_kernel<false, true, MERGE><<<grid, block, 0, stream>>>(a, c);
@@ -383,8 +439,37 @@ void launch_select_kernel(const SelectArgs& a, const CombineArgs& c, int extra_b
 
 }  // namespace
 
+bool select_two_stage(int max_len, int topk, int* chunk, int* nchunks) {
+  // From three chunks up: each launch has a fixed cost of about 12 us (its serial phases on one CU),
+  // which two chunks' parallel first stage does not win back (51200 positions, k = 2048: 33.2 us in
+  // two launches against 29.9 us in one; 102400 positions: 35.9 us against 46.2 us).
+  if (max_len <= 2 * kPerSuper || topk < 1) return false;
+  const int nc = (max_len + kPerSuper - 1) / kPerSuper;
+  // Equal chunks, each a multiple of 4 positions (16-byte aligned loads) and at most one super-round.
+  int c = (max_len + nc - 1) / nc;
+  c = (c + 3) / 4 * 4;
+  if (c > kPerSuper) return false;
+  const int n = (max_len + c - 1) / c;
+  if ((int64_t)n * topk > kPerSuper) return false;  // candidate row longer than one super-round
+  *chunk = c;
+  *nchunks = n;
+  return true;
+}
+
+// Stage arguments that the kernel's indexing relies on.
+bool stage_args_ok(const SelectArgs& a) {
+  if (a.stage == 0) return true;
+  if (a.stage != 1 && a.stage != 2) return false;
+  if (a.shared || a.unit_k || !a.cand_score || !a.cand_pos) return false;
+  if (a.chunk < 4 || a.chunk % 4 != 0 || a.chunk > kPerSuper || a.nchunks < 1) return false;
+  if ((int64_t)a.chunk * a.nchunks < a.max_len) return false;
+  if (a.cand_stride % 4 != 0 || a.cand_stride > kPerSuper || (int64_t)a.nchunks * a.topk > a.cand_stride) return false;
+  return (int64_t)a.batch * a.kv_heads * a.nchunks <= 0x7fffffff;
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
+  if (!stage_args_ok(a)) return hipErrorInvalidValue;
   launch_select_kernel<false>(a, CombineArgs{}, 0, stream);
   return hipGetLastError();
 }
@@ -392,6 +477,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
 hipError_t launch_select_merge(const SelectArgs& a, const CombineArgs& c, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
   if (c.rows <= 0) return launch_select(a, stream);
+  if (!stage_args_ok(a)) return hipErrorInvalidValue;
   if (c.splits < 1 || c.splits > kMaxSplitsPerUnit) return hipErrorInvalidValue;
   if (c.head_dim != 64 && c.head_dim != 128) return hipErrorInvalidValue;
   launch_select_kernel<true>(a, c, (c.rows + kWaves - 1) / kWaves, stream);

@@ -230,7 +230,7 @@ def test_select_topk_on_crafted_scores():
 def test_select_topk_paths(n, kind):
     """Register-resident rows (n <= 32768) and re-read rows: up to four super-rounds the output comes
     from the masks kept by the candidate pass (40000, 70000, 102400), beyond that from a third read
-    (140000); threshold bucket resolved by radix digits over its candidates (normal, two-values,
+    (140000); rows over 65536 also in two launches (chunks, then their winners); threshold bucket resolved by radix digits over its candidates (normal, two-values,
     cluster, huge: a range too wide for float32 puts every score in one bucket) or over all keys
     (tied, outlier: bucket larger than the LDS list)."""
     rng = np.random.default_rng(n)
@@ -256,17 +256,21 @@ def test_select_topk_paths(n, kind):
     else:
         s = rng.choice(np.array([1.0, 2.0], dtype=np.float32), size=(B, H, n))
     lens = np.array([n, n - 333], dtype=np.int32)
-    for k in (1, 257, 4096, n - 400):
-        idx = ppsa.select_topk(torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV), k)
-        torch.cuda.synchronize()
-        got = idx.cpu().numpy()
-        for b in range(B):
-            for h in range(H):
-                m = int(lens[b])
-                want = oracle.select_topk(s[b, h, :m], k)
-                g = got[b, h]
-                assert np.array_equal(np.sort(g[g >= 0]), np.sort(want[want >= 0])), (n, kind, k, b, h)
-                assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, m):] == -1)
+    # Rows over 65536 positions: both the two-launch form (top-k per chunk, then over the chunks'
+    # winners; used when a workspace is given and the winners fit one super-round) and one launch.
+    for two_stage in ((True, False) if n > 65536 else (True,)):
+        for k in (1, 257, 4096, n - 400):
+            idx = ppsa.select_topk(torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV), k,
+                                   two_stage=two_stage)
+            torch.cuda.synchronize()
+            got = idx.cpu().numpy()
+            for b in range(B):
+                for h in range(H):
+                    m = int(lens[b])
+                    want = oracle.select_topk(s[b, h, :m], k)
+                    g = got[b, h]
+                    assert np.array_equal(np.sort(g[g >= 0]), np.sort(want[want >= 0])), (n, kind, k, b, h, two_stage)
+                    assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, m):] == -1)
 
 
 FULL_SIZE_UNITS = {
