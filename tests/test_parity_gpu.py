@@ -273,6 +273,29 @@ def test_select_topk_paths(n, kind):
                     assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, m):] == -1)
 
 
+def test_select_two_launch_with_empty_and_partial_chunks():
+    """Two-launch selection (140000 positions: five chunks of 28000) on rows whose live lengths leave
+    whole chunks empty, one chunk partly live, and a budget above some chunks' live counts: the set is
+    the oracle's, bit for bit, and the same as the one-launch set."""
+    rng = np.random.default_rng(31)
+    B, H, N = 4, 2, 140000
+    s = (rng.standard_normal((B, H, N)) * 2).astype(np.float32)
+    s[1, :, 20000:20010] = 50.0  # ties among the largest, inside the only live chunk of row 1
+    lens = np.array([N, 30000, 56001, 28000], dtype=np.int32)
+    st, lt = torch.from_numpy(s).to(DEV), torch.from_numpy(lens).to(DEV)
+    for k in (1000, 4096, 6000):
+        two = ppsa.select_topk(st, lt, k, two_stage=True).cpu().numpy()
+        one = ppsa.select_topk(st, lt, k, two_stage=False).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(two, one), k
+        for b in range(B):
+            for h in range(H):
+                want = oracle.select_topk(s[b, h, :lens[b]], k)
+                g = two[b, h]
+                assert np.array_equal(np.sort(g[g >= 0]), np.sort(want[want >= 0])), (k, b, h)
+                assert np.all(np.diff(g[g >= 0]) > 0) and np.all(g[min(k, lens[b]):] == -1)
+
+
 FULL_SIZE_UNITS = {
     "llama3-8b-gqa-32k": [(0, 0), (1, 3), (2, 5), (3, 7)],
     "llama2-7b-10k": [(0, 0), (0, 17), (0, 31)],
