@@ -65,27 +65,29 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
 }
 
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,
-// at most 64 waves). `lds` needs NT/64 + 1 words. Returns the exclusive sum
-// and sets *total to the sum over the workgroup. Contains barriers: every
-// thread must call it.
+// at most 64 waves). Returns the exclusive sum and sets *total to the sum over
+// the workgroup. One barrier: each wave writes its total to one of two LDS
+// buffers (`lds` holds 2 * NT/64 words; `parity` picks the buffer and is
+// flipped, so consecutive calls alternate), and after the barrier every wave
+// scans the wave totals itself. A buffer is written again two calls later, by
+// which time every thread has passed the barrier of the call in between, so
+// all reads of it are done. Every thread must call it, with the same parity.
 template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* lds, uint32_t* total) {
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* lds, int& parity, uint32_t* total) {
   constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  uint32_t inc = wave_inclusive_scan(x);
-  if (lane == kWave - 1) lds[wave] = inc;
+  static_assert(NW >= 1 && NW <= kWave, "one to 64 waves");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  uint32_t* buf = lds + parity * NW;
+  parity ^= 1;
+  const uint32_t inc = wave_inclusive_scan(x);
+  if (lane == kWave - 1) buf[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < NW ? lds[lane] : 0u;
-    uint32_t wi = wave_inclusive_scan(w);
-    if (lane < NW) lds[lane] = wi - w;  // exclusive prefix of wave totals
-    if (lane == NW - 1) lds[NW] = wi;
-  }
-  __syncthreads();
-  uint32_t res = lds[wave] + inc - x;
-  *total = lds[NW];
-  __syncthreads();
-  return res;
+  const uint32_t w = lane < NW ? buf[lane] : 0u;
+  const uint32_t wi = wave_inclusive_scan(w);  // lanes < NW: inclusive prefix of the wave totals
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)wi, NW - 1);
+  const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)(wi - w), wave);
+  return before + inc - x;
 }
 
 }  // namespace ppsa

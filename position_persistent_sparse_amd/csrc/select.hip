@@ -69,14 +69,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // from the top) at which the running count reaches `remaining`, and
 // publishes it with the count of keys above it. Barriers inside.
 template <int BINS>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining, uint32_t* scan_lds,
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining, uint32_t* scan_lds, int& parity,
                                            uint32_t* digit, uint32_t* above_out) {
   constexpr int per = BINS / kThreads;  // 2 or 1
   const int tid = threadIdx.x;
   const int top = BINS - 1 - tid * per;
   const uint32_t c0 = hist[top], c1 = per == 2 ? hist[top - 1] : 0u;
   uint32_t total;
-  const uint32_t above = block_exclusive_scan<kThreads>(c0 + c1, scan_lds, &total);
+  const uint32_t above = block_exclusive_scan<kThreads>(c0 + c1, scan_lds, parity, &total);
   if (above < remaining && remaining <= above + c0) {
     *digit = (uint32_t)top;
     *above_out = above;
@@ -122,9 +122,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
       return;
     }
   }
-  __shared__ uint32_t hist[kBins + 1];  // bin kBins absorbs padding slots
-  __shared__ uint32_t histc[(kBins + 1) * kCopies];
-  __shared__ uint32_t scan_lds[kWaves + 1];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t histc[kBins * kCopies];
+  __shared__ uint32_t scan_lds[2 * kWaves];
+  int parity = 0;  // scan buffer (block_exclusive_scan alternates two)
   __shared__ uint32_t cand[kMaxCand];
   __shared__ uint32_t s_digit, s_above;
 
@@ -262,17 +263,17 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
     }
   };
 
-  // 1. Digit 1 over all keys (padding slots count into the spare bin).
-  for (int i = tid; i < (kBins + 1) * kCopies; i += kThreads) histc[i] = 0u;
+  // 1. Digit 1 over all live keys.
+  for (int i = tid; i < kBins * kCopies; i += kThreads) histc[i] = 0u;
   __syncthreads();
   const uint32_t copy = (uint32_t)(lane % kCopies);
   for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
 #pragma unroll
     for (int i = 0; i < kCached; ++i)
-      if (i < sp.per) atomicAdd(&histc[(((sp.live >> i) & 1u) ? (k[i] >> 21) : (uint32_t)kBins) * kCopies + copy], 1u);
+      if (i < sp.per && ((sp.live >> i) & 1u)) atomicAdd(&histc[(k[i] >> 21) * kCopies + copy], 1u);
   });
   __syncthreads();
-  for (int i = tid; i <= kBins; i += kThreads) {
+  for (int i = tid; i < kBins; i += kThreads) {
     uint32_t c = 0u;
 #pragma unroll
     for (int j = 0; j < kCopies; ++j) c += histc[i * kCopies + j];
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   }
   __syncthreads();
   uint32_t remaining = (uint32_t)k_eff;
-  find_digit<kBins>(hist, remaining, scan_lds, &s_digit, &s_above);
+  find_digit<kBins>(hist, remaining, scan_lds, parity, &s_digit, &s_above);
   uint32_t prefix = s_digit << 21;
   uint32_t mask = 0xFFE00000u;
   remaining -= s_above;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
         }
       cm &= sp.live;
       uint32_t total;
-      uint32_t slot = base + block_exclusive_scan<kThreads>(__popc(cm), scan_lds, &total);
+      uint32_t slot = base + block_exclusive_scan<kThreads>(__popc(cm), scan_lds, parity, &total);
       const Marks marks{abv & sp.live, cm, slot};
 #pragma unroll
       for (int i = 0; i < kCached; ++i)
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
     const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
-    for (int i = tid; i <= kBins; i += kThreads) hist[i] = 0u;
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
     if (use_cand) {
       for (uint32_t i = tid; i < n_cand; i += kThreads) {
@@ -357,12 +358,14 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
       });
     }
     __syncthreads();
-    if (pass == 0) find_digit<2048>(hist, remaining, scan_lds, &s_digit, &s_above);
-    else find_digit<1024>(hist, remaining, scan_lds, &s_digit, &s_above);
+    if (pass == 0) find_digit<2048>(hist, remaining, scan_lds, parity, &s_digit, &s_above);
+    else find_digit<1024>(hist, remaining, scan_lds, parity, &s_digit, &s_above);
+    // s_digit and s_above are next written by the next find_digit, after the next pass's barriers,
+    // which every thread reaches only after reading them here; hist is read inside find_digit
+    // before its scan's barrier, so the next pass may clear it.
     prefix |= s_digit << shift;
     mask |= dmask << shift;
     remaining -= s_above;
-    __syncthreads();
   }
   const uint32_t thresh = prefix;
   const uint32_t needed_eq = remaining;  // >= 1 keys equal to thresh, lowest positions first
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
     // One scan of both counts: per super-round each total is at most 32768, so the counts of keys
     // == T (low 16 bits) never carry into those of keys > T (high 16 bits).
     uint32_t tot;
-    const uint32_t before = block_exclusive_scan<kThreads>((n_gt << 16) | n_eq, scan_lds, &tot);
+    const uint32_t before = block_exclusive_scan<kThreads>((n_gt << 16) | n_eq, scan_lds, parity, &tot);
     const uint32_t gt_before = gt_seen + (before >> 16), eq_before = eq_seen + (before & 0xFFFFu);
     const uint32_t tot_gt = tot >> 16, tot_eq = tot & 0xFFFFu;
     // Saturating forms only: hipcc 7.2 turned a guarded `needed - before` feeding min() into an
