@@ -50,7 +50,7 @@ __device__ __forceinline__ void store_out4(uint16_t* p, float4_t o, float inv) {
 template <int WAVES, bool STREAM>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_sparse_kernel(AttnArgs a) {
   constexpr int kThreads = WAVES * kWave;
-  extern __shared__ float dyn[];  // [WAVES] wave regions: K block during the tile loop, then the wave's O
+  extern __shared__ __attribute__((aligned(16))) float dyn[];  // [WAVES] wave regions: K block during the tile loop, then the wave's O
   __shared__ float sm_m[WAVES][kMaxGroup];
   __shared__ float sm_l[WAVES][kMaxGroup];
   const int group = a.group, S = a.splits;
