@@ -119,14 +119,22 @@ __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[blk][j] = ((cur.valid >> (4 * blk + j)) & 1u) ? s[blk][j] * a.scale_log2 : -INFINITY;
     if constexpr (MODE == MODE_FULL_HEADS) {
-      // Every query head's logit of the tile's live rows: lane (g, n < group) holds rows 16 blk + 4g + j.
+      // Every query head's logit of the tile's live rows: lane (g, n < group) holds rows 16 blk + 4g + j,
+      // four consecutive rows: one 16-byte store when all four are live and the row start allows it.
       if (n < group) {
         float* hl = a.head_logits + ((size_t)b * a.q_heads + (size_t)kv * group + n) * a.max_len + slot0 + ti * kTile;
+        const bool vec = (a.max_len % 4) == 0 && (reinterpret_cast<uintptr_t>(a.head_logits) % 16) == 0;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk) {
+          float* p = hl + 16 * blk + 4 * g;
+          if (vec && ((cur.valid >> (4 * blk)) & 0xFu) == 0xFu) {
+            *reinterpret_cast<float4*>(p) = make_float4(x[blk][0], x[blk][1], x[blk][2], x[blk][3]);
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if ((cur.valid >> (4 * blk + j)) & 1u) hl[16 * blk + 4 * g + j] = x[blk][j];
+            for (int j = 0; j < 4; ++j)
+              if ((cur.valid >> (4 * blk + j)) & 1u) p[j] = x[blk][j];
+          }
+        }
       }
     }
     softmax_pv(cur, x, st, g);
