@@ -428,14 +428,15 @@ def test_select_topk_shared_exact(n):
                 assert np.array_equal(got[b, h], np.sort(want[want >= 0]).tolist() + [-1] * (k - min(k, m))), (n, k, b, h)
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "llama3-8b-gqa-32k", "llama3-70b-ragged-10k"])
+@pytest.mark.parametrize("name", ["tiny-f32", "llama3-8b-gqa-32k", "llama3-70b-ragged-10k", "llama2-7b-10k"])
 def test_decode_step_softmax_selection(name):
     """Softmax-weight selection (a group ranks a position by the sum of its heads' softmax weights). The
     written scores are within 1e-4 relative of the oracle's (logits carry ~1e-6 relative float32 error,
     exp2 and the normaliser about as much, so 1e-4 leaves a tenfold margin); the set passes the band
     rule with a band of 1e-4 of s_k and is exactly the top-k of its own scores; outputs are checked
     layer by layer, sparse layers against the GPU's own set. Covers the vector-ALU path (fp32, group 1),
-    split and single-split matrix-core launches (groups 4 and 8)."""
+    split and single-split matrix-core launches (groups 4 and 8), and group 1 with a row length that is
+    not a multiple of 4 (3001: head logits and scores stored one float at a time)."""
     wl = REDUCED[name]
     gen = synth.Generator(wl)
     say(f"[parity] softmax selection {name}: lens={gen.seq_lens.tolist()}")
