@@ -35,7 +35,9 @@
  *   - Errors: every argument is checked on the host before any HIP call. A
  *     failing check returns a negative ppsa_status and enqueues nothing. A
  *     failed launch returns PPSA_ERR_HIP. The library never aborts or throws.
- *   - Calls are stateless. Concurrent calls must use distinct workspaces.
+ *   - Method calls keep no state between calls (the instruments at the end --
+ *     launch timing, the split-planner override -- are process-wide
+ *     settings). Concurrent calls must use distinct workspaces.
  */
 #ifndef PPSA_H
 #define PPSA_H
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PPSA_ABI_VERSION 1
+#define PPSA_ABI_VERSION 2
 
 typedef enum ppsa_status {
   PPSA_OK = 0,
@@ -73,7 +75,8 @@ typedef struct ppsa_dims {
   float scale;          /* logit scale; 0 means 1/sqrt(head_dim) */
 } ppsa_dims;
 
-/* Library ABI version (PPSA_ABI_VERSION). */
+/* Library ABI version (PPSA_ABI_VERSION). 2: ppsa_append_kv takes the dropped-token counter;
+ * ppsa_sparse_attn_phases, ppsa_decode_step_static, ppsa_set_split_rows and the probes added. */
 int ppsa_abi_version(void);
 
 /* Static text for a status code. */

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ppsa.abi_version() == 1
+    assert ppsa.abi_version() == 2
     assert ppsa.status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5, -6):
         assert ppsa.status_string(code) not in ("ok", "unknown status")
