@@ -203,6 +203,10 @@ def test_select_mode_validation():
     # A valid mode reaches the usual checks (idx misaligned for int32 here, so nothing is launched).
     assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, ppsa.PPSA_SELECT_SHARED,
                                    ctypes.c_void_p(0x100002), None, 0, None) == ppsa.PPSA_ERR_INVALID_ARG
+    # The optional workspace: a size without a pointer, or a pointer not 16-byte aligned.
+    for ws, nbytes in ((None, 4096), (ctypes.c_void_p(0x100004), 1 << 30)):
+        assert LIB.ppsa_select_topk_ex(ctypes.byref(d), FAKE, FAKE, 16, ppsa.PPSA_SELECT_PER_KV_HEAD, FAKE, ws,
+                                       nbytes, None) == ppsa.PPSA_ERR_INVALID_ARG, (ws, nbytes)
 
 
 def test_binding_rejects_mismatched_buffers():
