@@ -92,6 +92,15 @@ WORKLOADS = {
     "llama3-70b-ragged-10k": Workload("llama3-70b-ragged-10k", layers=80, batch=8, q_heads=64, kv_heads=8,
                                       head_dim=128, max_len=10240, min_len=8192, topk=256, dtype="bf16",
                                       select_layers=(2, 14), seed=1005),
+    # One GPU's share of the two GQA shapes under 8-way sharding over KV heads (every GPU holds one KV
+    # head and its query heads for the whole batch; attention and selection need no exchange). Same
+    # seed as the whole shape: the inputs and lengths are exactly its KV head 0 and query heads 0..g-1.
+    "llama3-8b-gqa-32k-tp8": Workload("llama3-8b-gqa-32k-tp8", layers=32, batch=4, q_heads=4, kv_heads=1,
+                                      head_dim=128, max_len=32768, topk=4096, dtype="bf16",
+                                      select_layers=(2, 14), seed=1003),
+    "llama3-70b-ragged-10k-tp8": Workload("llama3-70b-ragged-10k-tp8", layers=80, batch=8, q_heads=8, kv_heads=1,
+                                          head_dim=128, max_len=10240, min_len=8192, topk=256, dtype="bf16",
+                                          select_layers=(2, 14), seed=1005),
 }
 
 # The workload the benchmark times by default: the LLaMA-3-8B GQA shape at 32K.

@@ -43,3 +43,23 @@ def test_step_bytes_ragged():
     per_full = 2 * wl.batch * wl.kv_heads * 9216 * 256
     per_sparse = 2 * wl.batch * wl.kv_heads * 256 * 256
     assert step_kv_bytes(wl, lens) == 4 * per_full + 76 * per_sparse == 1845493760
+
+
+def test_sharded_workloads_are_kv_head_zero_of_their_shape():
+    """The 8-way KV-head shards reproduce the whole shape's KV head 0 and its query heads bit for bit
+    (same seed, counter-based generator), so their timings are one GPU's share of that shape."""
+    from synth import Generator
+    for shard, whole in (("llama3-8b-gqa-32k-tp8", "llama3-8b-gqa-32k"),
+                         ("llama3-70b-ragged-10k-tp8", "llama3-70b-ragged-10k")):
+        kw = dict(layers=4, max_len=2048, topk=256)
+        ws, ww = WORKLOADS[shard], WORKLOADS[whole]
+        if ww.ragged:
+            kw["min_len"] = 1500
+        gs, gw = Generator(ws.with_(**kw)), Generator(ww.with_(**kw))
+        assert ws.kv_heads == 1 and ws.q_heads == ww.group and ws.batch == ww.batch
+        assert gs.seq_lens.tolist() == gw.seq_lens.tolist()
+        layer = 3
+        assert np.array_equal(gs.q(layer), gw.q(layer)[:, :ws.q_heads])
+        ks, vs = gs.kv(layer, None, None)
+        kw_, vw = gw.kv(layer, None, None)
+        assert np.array_equal(ks, kw_[:, :1]) and np.array_equal(vs, vw[:, :1])

@@ -301,6 +301,8 @@ FULL_SIZE_UNITS = {
     "llama2-7b-10k": [(0, 0), (0, 17), (0, 31)],
     "llama2-7b-100k": [(0, 0), (0, 21)],
     "llama3-70b-ragged-10k": [(0, 0), (3, 4), (7, 7)],
+    "llama3-8b-gqa-32k-tp8": [(0, 0), (3, 0)],
+    "llama3-70b-ragged-10k-tp8": [(1, 0), (6, 0)],
 }
 
 
