@@ -28,9 +28,12 @@
 //     prefix sum of the packed counts gives its first output slot, and it
 //     writes its kept positions in order by walking the set bits.
 // Rows of one super-round keep their keys in registers through all steps;
-// longer rows reload their super-rounds in each step, except that rows of up
-// to four super-rounds take step 3 from masks kept by step 2 (two reads of
-// the scores instead of three).
+// longer rows reload their super-rounds in each step. When the threshold bin
+// fits in LDS, step 3 works from the masks step 2 kept (in registers for one
+// super-round, in LDS for up to four) and the candidates' keys, so no step
+// after 2 passes over every key again. The work is bound by instruction issue
+// on the one CU (16 waves on 4 SIMDs), so the per-key steps carry no per-key
+// branch or test beyond their arithmetic.
 //
 // Rows of more than two super-rounds may instead be taken in two launches
 // (SelectArgs::stage): the same kernel first runs on chunks of the row, one
@@ -199,14 +202,15 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   // Super-round r spans n_r positions; thread t owns per_r of them from p0(r, t) = 32768 r + t per_r,
   // per_r = ceil(n_r / 1024) rounded up to a multiple of 4 (so that full spans load 16 bytes at a
   // time; the last threads may own fewer or none). Loads this thread's keys (0 past its live ones)
-  // and the mask of the live ones.
+  // and the mask of the live ones. per_r is the same for every thread: the steps below skip keys
+  // past it four at a time on a scalar branch and mask the rest with `live`, with no per-key test.
   struct Span {
     int p0, per;
     uint32_t live;
   };
   auto span_of = [&](int r) -> Span {
     const int n_r = min(kPerSuper, n - r * kPerSuper);
-    const int per = ((n_r + kThreads - 1) / kThreads + 3) & ~3;
+    const int per = __builtin_amdgcn_readfirstlane(((n_r + kThreads - 1) / kThreads + 3) & ~3);
     const int p0 = r * kPerSuper + tid * per;
     const int cnt = max(0, min(per, r * kPerSuper + n_r - p0));
     return Span{p0, per, cnt >= kCached ? 0xFFFFFFFFu : ((1u << cnt) - 1u)};
@@ -232,20 +236,33 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
           k[4 * j + 1] = order_key(f.y);
           k[4 * j + 2] = order_key(f.z);
           k[4 * j + 3] = order_key(f.w);
+        } else {
+          k[4 * j] = k[4 * j + 1] = k[4 * j + 2] = k[4 * j + 3] = 0u;
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < kCached; ++i)
-        if (i < per) {
-          float f = 0.0f;
-          if (i < cnt) {
-            f = s[p0 + i];
-            for (int r = 1; r < rows; ++r) f += s[(size_t)r * pitch + p0 + i];
-          }
-          k[i] = i < cnt ? order_key(f) : 0u;
+      for (int i = 0; i < kCached; ++i) {
+        float f = 0.0f;
+        if (i < cnt) {
+          f = s[p0 + i];
+          for (int r = 1; r < rows; ++r) f += s[(size_t)r * pitch + p0 + i];
         }
+        k[i] = i < cnt ? order_key(f) : 0u;
+      }
     }
     return Span{p0, per, live};
+  };
+  // fn(i) for this thread's keys i < per_r, four at a time on a scalar branch (per_r is a multiple
+  // of 4 and the same for every thread).
+  auto for_keys = [&](const Span& sp, auto&& fn) {
+#pragma unroll
+    for (int j = 0; j < kCached / 4; ++j)
+      if (4 * j < sp.per) {
+        fn(4 * j);
+        fn(4 * j + 1);
+        fn(4 * j + 2);
+        fn(4 * j + 3);
+      }
   };
   uint32_t keys[CACHED ? kCached : 1];
   Span span{0, 0, 0u};
@@ -268,9 +285,8 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   __syncthreads();
   const uint32_t copy = (uint32_t)(lane % kCopies);
   for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
-#pragma unroll
-    for (int i = 0; i < kCached; ++i)
-      if (i < sp.per && ((sp.live >> i) & 1u)) atomicAdd(&histc[(k[i] >> 21) * kCopies + copy], 1u);
+    // Each key adds its live bit (a dead key adds 0 to bin 0): no branch per key.
+    for_keys(sp, [&](int i) { atomicAdd(&histc[(k[i] >> 21) * kCopies + copy], (sp.live >> i) & 1u); });
   });
   __syncthreads();
   for (int i = tid; i < kBins; i += kThreads) {
@@ -290,40 +306,41 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
   __syncthreads();
 
   // 2. Digits 2 and 3, over the candidates (or over all keys if they do not fit).
-  // Rows re-read from memory in every pass (longer than one super-round) but of at most kMaskSR
-  // super-rounds: the candidate pass also keeps, per super-round, the bit masks of this thread's
-  // keys above the threshold bin and in it, and where its candidates went in `cand`; the output
-  // step then needs only those and the candidates, not a third read of the scores.
-  const bool keep_masks = !CACHED && use_cand && n_sr <= kMaskSR;
+  // The candidate pass also keeps, per super-round, the bit masks of this thread's keys above the
+  // threshold bin and in it, and where its candidates went in `cand` (in registers for rows of one
+  // super-round; in LDS for rows of up to kMaskSR, which are re-read from memory in every pass); the
+  // output step then needs only those and the candidates, not another pass over every key.
+  const bool keep_masks = use_cand && (CACHED || n_sr <= kMaskSR);
   // [super-round][above, cand, first cand slot][thread], in LDS: registers are at their limit here.
   __shared__ uint32_t sm_marks[CACHED ? 1 : kMaskSR * 3 * kThreads];
   auto mark = [&](int r, int f) -> uint32_t& { return sm_marks[(r * 3 + f) * kThreads + tid]; };
+  struct Marks {
+    uint32_t above, cand, at;
+  };
+  Marks reg_marks{0u, 0u, 0u};  // rows of one super-round
   if (use_cand) {
     // Each thread marks its candidates in a bit mask; one workgroup scan of the counts gives its
     // first slot in `cand` (candidates taken in position order, no atomics on a shared counter).
     uint32_t base = 0u;
-    struct Marks {
-      uint32_t above, cand, at;
-    };
     auto collect = [&](const uint32_t(&k)[kCached], const Span& sp) -> Marks {
       uint32_t cm = 0u, abv = 0u;
-#pragma unroll
-      for (int i = 0; i < kCached; ++i)
-        if (i < sp.per) {
-          cm |= (uint32_t)((k[i] & mask) == prefix) << i;
-          abv |= (uint32_t)((k[i] & mask) > prefix) << i;
-        }
+      for_keys(sp, [&](int i) {
+        cm |= (uint32_t)((k[i] & mask) == prefix) << i;
+        abv |= (uint32_t)((k[i] & mask) > prefix) << i;
+      });
       cm &= sp.live;
       uint32_t total;
       uint32_t slot = base + block_exclusive_scan<kThreads>(__popc(cm), scan_lds, parity, &total);
       const Marks marks{abv & sp.live, cm, slot};
-#pragma unroll
-      for (int i = 0; i < kCached; ++i)
+      for_keys(sp, [&](int i) {
         if ((cm >> i) & 1u) cand[slot++] = k[i];
+      });
       base += total;
       return marks;
     };
-    if (keep_masks) {
+    if constexpr (CACHED) {
+      reg_marks = collect(keys, span);
+    } else if (keep_masks) {
 #pragma unroll
       for (int r = 0; r < kMaskSR; ++r)
         if (r < n_sr) {  // the same for every thread
@@ -351,10 +368,9 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
       }
     } else {
       for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
-#pragma unroll
-        for (int i = 0; i < kCached; ++i)
-          if (i < sp.per && ((sp.live >> i) & 1u) && (k[i] & mask) == prefix)
-            atomicAdd(&hist[(k[i] >> shift) & dmask], 1u);
+        for_keys(sp, [&](int i) {
+          if (((sp.live >> i) & 1u) && (k[i] & mask) == prefix) atomicAdd(&hist[(k[i] >> shift) & dmask], 1u);
+        });
       });
     }
     __syncthreads();
@@ -372,6 +388,48 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
 
   // 3. Output in position order (super-round, thread, bit), from each thread's masks of keys > T
   //    and == T.
+  // Writes the positions p0 + (set bits of `take`, lowest first) to slots slot, slot + 1, ...
+  // Stage 0 stores positions only; stages 1 and 2 also load a value per position (its score, its
+  // original position): eight loads in flight before their stores, not one round trip each.
+  auto emit_bits = [&](uint32_t take, uint32_t slot, int p0) {
+    if (stage == 0) {
+      for (; take != 0u; take &= take - 1u, ++slot) {
+        const int32_t p = p0 + __ffs(take) - 1;
+        for (int r = 0; r < rows; ++r) out[(size_t)r * a.topk + slot] = p;
+      }
+      return;
+    }
+    constexpr int kBatch = 8;
+    while (take != 0u) {
+      int pos[kBatch];
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        pos[j] = take != 0u ? p0 + __ffs(take) - 1 : p0;
+        cnt += take != 0u ? 1 : 0;
+        take &= take - 1u;
+      }
+      if (stage == 1) {
+        float v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = j < cnt ? s[pos[j]] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          if (j < cnt) {
+            cand_score[slot + j] = v[j];
+            cand_pos[slot + j] = pos0 + pos[j];
+          }
+      } else {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) v[j] = j < cnt ? pos_map[pos[j]] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          if (j < cnt) out[slot + j] = v[j];
+      }
+      slot += (uint32_t)cnt;
+    }
+  };
   uint32_t gt_seen = 0u, eq_seen = 0u;  // over earlier super-rounds
   auto emit_sr = [&](uint32_t gtm, uint32_t eqm, const Span& sp) {
     const uint32_t n_gt = __popc(gtm), n_eq = __popc(eqm);
@@ -384,38 +442,36 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(SelectArgs a, Com
     // Saturating forms only: hipcc 7.2 turned a guarded `needed - before` feeding min() into an
     // unconditional one assumed not to wrap, which dropped the clamp on the slot below.
     const uint32_t room = max(needed_eq, eq_before) - eq_before;  // keys == T this thread may take
-    uint32_t take = gtm | lowest_bits(eqm, min(room, n_eq));
-    uint32_t slot = gt_before + (needed_eq - room);              // + min(eq_before, needed_eq)
-    while (take) {
-      emit(slot++, sp.p0 + __ffs(take) - 1);
-      take &= take - 1u;
-    }
+    emit_bits(gtm | lowest_bits(eqm, min(room, n_eq)), gt_before + (needed_eq - room), sp.p0);
     gt_seen += tot_gt;
     eq_seen += tot_eq;
   };
+  // From the candidate pass's masks: keys above the threshold bin are kept, and candidates are
+  // compared with T as `cand` holds them (this thread's, in bit order from its first slot).
+  auto emit_marks = [&](uint32_t above, uint32_t cm, uint32_t at, const Span& sp) {
+    uint32_t gtm = above, eqm = 0u;
+    for (; cm != 0u; cm &= cm - 1u) {
+      const uint32_t key = cand[at++], bit = cm & (0u - cm);
+      if (key > thresh) gtm |= bit;
+      else if (key == thresh) eqm |= bit;
+    }
+    emit_sr(gtm, eqm, sp);
+  };
   if (keep_masks) {
+    if constexpr (CACHED) {
+      emit_marks(reg_marks.above, reg_marks.cand, reg_marks.at, span);
+    } else {
 #pragma unroll
-    for (int r = 0; r < kMaskSR; ++r)
-      if (r < n_sr) {
-        // Keys above the threshold bin are kept; candidates are compared with T as `cand` holds them
-        // (this thread's, in bit order from cand_at[r]).
-        uint32_t gtm = mark(r, 0), eqm = 0u, at = mark(r, 2);
-        for (uint32_t m = mark(r, 1); m != 0u; m &= m - 1u) {
-          const uint32_t key = cand[at++], bit = m & (0u - m);
-          if (key > thresh) gtm |= bit;
-          else if (key == thresh) eqm |= bit;
-        }
-        emit_sr(gtm, eqm, span_of(r));
-      }
+      for (int r = 0; r < kMaskSR; ++r)
+        if (r < n_sr) emit_marks(mark(r, 0), mark(r, 1), mark(r, 2), span_of(r));
+    }
   } else {
     for_sr([&](const uint32_t(&k)[kCached], const Span& sp) {
       uint32_t gtm = 0u, eqm = 0u;
-#pragma unroll
-      for (int i = 0; i < kCached; ++i)
-        if (i < sp.per) {
-          gtm |= (uint32_t)(k[i] > thresh) << i;
-          eqm |= (uint32_t)(k[i] == thresh) << i;
-        }
+      for_keys(sp, [&](int i) {
+        gtm |= (uint32_t)(k[i] > thresh) << i;
+        eqm |= (uint32_t)(k[i] == thresh) << i;
+      });
       emit_sr(gtm & sp.live, eqm & sp.live, sp);
     });
   }
