@@ -48,7 +48,7 @@ EVICT_BYTES = 1 << 30  # read between per-step timings: larger than the last-lev
 # Sources of the attention kernels: HBM traffic counted for a kernel holds only while they are unchanged.
 ATTN_SOURCES = ("attn_mfma.hip", "attn_sparse.hip", "mfma_tile.h", "sparse_gather.h", "attn_epilogue.h",
                 "device_common.h", "ppsa_internal.h")
-# Host threads the oracle may use: the GPU's share of the host (16 per GPU on the boxes this runs on).
+# Host threads the oracle may use: at most 16, one GPU's share of a multi-GPU host.
 CPU_THREADS_CAP = 16
 
 

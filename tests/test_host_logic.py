@@ -63,3 +63,15 @@ def test_sharded_workloads_are_kv_head_zero_of_their_shape():
         ks, vs = gs.kv(layer, None, None)
         kw_, vw = gw.kv(layer, None, None)
         assert np.array_equal(ks, kw_[:, :1]) and np.array_equal(vs, vw[:, :1])
+
+
+def test_hbm_traffic_record_matches_the_attention_sources():
+    """The committed FETCH_SIZE / WRITE_SIZE record of the headline sparse kernel was taken on the
+    attention sources as they are now (their sha256 is stored with it and checked by the benchmark), and
+    it counts close to the algorithmic bytes: 2 k d e per (batch row, KV head), 32 units, plus slot
+    entries, q and partials. A change to those sources has to come with new counters."""
+    import bench
+    nbytes, source = bench.measured_traffic("llama3-8b-gqa-32k", "attn_sparse")
+    assert nbytes is not None, source
+    algorithmic = 2 * 4 * 8 * 4096 * 128 * 2
+    assert 1.0 <= nbytes / algorithmic < 1.1, nbytes / algorithmic
