@@ -500,8 +500,9 @@ void launch_select_kernel(const SelectArgs& a, const CombineArgs& c, int extra_b
 
 bool select_two_stage(int max_len, int topk, int* chunk, int* nchunks) {
   // From three chunks up: each launch has a fixed cost (its serial phases on one CU), which two
-  // chunks' parallel first stage did not win back when measured (51200 positions, k = 2048: 33.2 us
-  // in two launches against 29.9 us in one; 102400 positions: 35.9 us against 46.2 us).
+  // chunks' parallel first stage barely wins back (36000 to 65536 positions: 2-10 % faster in two
+  // launches for k <= 2048, 10-20 % slower for k = 4096); at 102400 positions two launches take
+  // 29 us against 47 us in one.
   if (max_len <= 2 * kPerSuper || topk < 1) return false;
   const int nc = (max_len + kPerSuper - 1) / kPerSuper;
   // Equal chunks, each a multiple of 4 positions (16-byte aligned loads) and at most one super-round.
