@@ -6,8 +6,8 @@ inputs resident in HBM, and prints one JSON line.
 
 Headline (`value`, `ms_per_step`): the workload the metric is quoted on
 (LLaMA-3-8B GQA, 32K context): K steps, each preceded (outside its HIP
-events) by a 1 GiB read that evicts the last-level cache and the L2s,
-reported as the median; `value` is the algorithmic K+V
+events) by two reads of a 1 GiB buffer that evict the last-level cache and
+the L2s, reported as the median; `value` is the algorithmic K+V
 bytes of one step over that median. The same K steps back to back without
 eviction are reported beside it (`step_us_back_to_back`).
 
@@ -23,7 +23,8 @@ summary of the timed outputs on sampled (batch row, KV head) units against
 the float64 oracle; the oracle itself timed on the host cores
 (`cpu_baseline`); comparison schedules, selection variants and a multi-token
 decode on the headline workload; and `workloads`: the other four
-configurations timed the same way.
+configurations and one GPU's share of the two GQA shapes under 8-way KV-head
+sharding, timed the same way.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--workloads all|none|NAME,...]
                     [--no-cpu-baseline] [--no-probes] [--no-parity] [--no-graph] [--no-comparison]
