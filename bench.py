@@ -16,7 +16,8 @@ The line also carries: per-kernel durations from the library's launch timing
 (attention launch plus its merge launch, and the two launches apart, each
 back to back in a captured graph); the roofline of the dominant kernel
 against the 8 TB/s peak and against the read bandwidth this GPU reaches
-(`roofline.achievable`, from the read probe), its duration taken from the
+(`roofline.achievable`, from the read probe; `achievable_same_size`, a read
+of the launch's own size), its duration taken from the
 graph of its launches (an event pair around every launch adds its marker
 packets to the launch); the sparse kernel over its load-only twin; measurement probes (read ceiling, launch floor); a parity
 summary of the timed outputs on sampled (batch row, KV head) units against
@@ -726,11 +727,18 @@ def main():
     else:
         us_launch, timing_src = kernels[dom]["us_per_launch"], "library launch timing (events around each launch)"
     achieved = round(nbytes / us_launch / 1e3, 1)
+    # The read ceiling at this launch's own size (a 64 MiB read back to back in a graph: one launch's ramp and
+    # drain included), when the probe read that many bytes.
+    same_size = None
+    if probes is not None and nbytes == 64 << 20:
+        same_size = probes["read_64MiB_nontemporal"]["GB_per_s"]
     roofline = {"bound": "hbm", "kernel": f"{dom}: {bench.ppsa.timing_kernel_name(bench.ppsa.KERNEL_KEYS.index(dom))}",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_source": traffic_src,
                 "achievable": achievable,
                 "frac_of_achievable": None if achievable is None else round(achieved / achievable, 4),
+                "achievable_same_size": same_size,
+                "frac_of_achievable_same_size": None if same_size is None else round(achieved / same_size, 4),
                 "bytes_per_launch": nbytes, "us_per_launch": us_launch, "us_per_launch_timing": timing_src,
                 "us_per_launch_event_pairs": kernels[dom]["us_per_launch"],
                 "launches_per_step": kernels[dom]["launches_per_step"]}
